@@ -1,0 +1,37 @@
+"""Error metrics (oracle; test infrastructure only)."""
+
+import numpy as np
+
+
+def sqnr_db(ref, out):
+    """Signal-to-quantization-noise ratio in dB: 20 log10(|ref| / |ref - out|).
+
+    [GENERIC] review thread asks for SQNR in the numerics tests; [REPRO]
+    Findings So Far prints SQNR values next to the norms they come from
+    (the printed collapse SQNRs follow from the printed norms under this
+    formula; tests/golden pins that).  Frobenius norms, float64.
+    """
+    ref = np.asarray(ref, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    num = np.linalg.norm(ref)
+    den = np.linalg.norm(ref - out)
+    if den == 0:
+        return float("inf")
+    return float(20.0 * np.log10(num / den))
+
+
+def rel_frobenius(ref, out):
+    """|ref - out|_F / |ref|_F in float64."""
+    ref = np.asarray(ref, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    n = np.linalg.norm(ref)
+    return float(np.linalg.norm(ref - out) / n) if n else float(np.linalg.norm(out))
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (float64): 2^(floor(log2|x|) - 7);
+    below the normal range, the subnormal spacing 2^-133."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, ex = np.frexp(a)
+    e = np.maximum(ex.astype(np.int64) - 1, -126)
+    return np.ldexp(1.0, e - 7)
