@@ -1,0 +1,414 @@
+// C ABI of libfp8bw.so: argument validation, workspace layout and kernel
+// dispatch.  Declarations and the contract of every entry point are in
+// include/fp8bw.h.  Validation is pure host code and runs before any HIP
+// call, so a rejected call enqueues nothing.
+
+#include "../../include/fp8bw.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+#define FP8BW_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int ok() {
+  g_err.clear();
+  return FP8BW_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FP8BW_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;   // int32 indexing inside the kernels
+constexpr int64_t kMaxGridY = 65535;
+
+// A strided 2-D scale grid [ni, nj] with strides (si, sj) must map distinct
+// index pairs to distinct addresses.
+bool strides_injective(int64_t ni, int64_t nj, int64_t si, int64_t sj) {
+  if (si < 0 || sj < 0) return false;
+  if (ni <= 1 && nj <= 1) return true;
+  if (ni <= 1) return sj >= 1;
+  if (nj <= 1) return si >= 1;
+  return (si >= 1 && sj >= si * ni) || (sj >= 1 && si >= sj * nj);
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+FP8BW_API int fp8bw_abi_version(void) { return 1; }
+
+FP8BW_API const char* fp8bw_status_str(int s) {
+  switch (s) {
+    case FP8BW_OK: return "FP8BW_OK";
+    case FP8BW_ERR_NULL: return "FP8BW_ERR_NULL";
+    case FP8BW_ERR_SHAPE: return "FP8BW_ERR_SHAPE";
+    case FP8BW_ERR_LAYOUT: return "FP8BW_ERR_LAYOUT";
+    case FP8BW_ERR_ALIGN: return "FP8BW_ERR_ALIGN";
+    case FP8BW_ERR_UNSUPPORTED: return "FP8BW_ERR_UNSUPPORTED";
+    case FP8BW_ERR_WORKSPACE: return "FP8BW_ERR_WORKSPACE";
+    case FP8BW_ERR_HIP: return "FP8BW_ERR_HIP";
+    default: return "FP8BW_ERR_UNKNOWN";
+  }
+}
+
+FP8BW_API const char* fp8bw_last_error(void) { return g_err.c_str(); }
+
+// ---------------------------------------------------------------------------
+// Quantization.
+
+static int check_quant_common(const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* q,
+                              int64_t ld_q, int64_t q_row_len) {
+  if (rows < 0 || cols < 0) return fail(FP8BW_ERR_SHAPE, "negative rows/cols (%lld, %lld)",
+                                        (long long)rows, (long long)cols);
+  if (rows > kMaxDim * 4 || cols > kMaxDim) return fail(FP8BW_ERR_SHAPE, "dimension too large");
+  if (cols % 16) return fail(FP8BW_ERR_SHAPE, "cols=%lld must be a multiple of 16", (long long)cols);
+  if (rows == 0 || cols == 0) return FP8BW_OK;
+  if (!x || !q) return fail(FP8BW_ERR_NULL, "x and q must be non-null");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(FP8BW_ERR_ALIGN, "x and q must be 16-byte aligned");
+  if (ld_x < cols || ld_x % 8) return fail(FP8BW_ERR_LAYOUT, "ld_x=%lld must be >= cols and a multiple of 8", (long long)ld_x);
+  if (ld_q < q_row_len || ld_q % 16)
+    return fail(FP8BW_ERR_LAYOUT, "ld_q=%lld must be >= %lld and a multiple of 16", (long long)ld_q, (long long)q_row_len);
+  return FP8BW_OK;
+}
+
+FP8BW_API int fp8_blockwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  int block, int transpose, void* q, int64_t ld_q, float* recip,
+                                  int64_t rs_row, int64_t rs_kb, void* stream) {
+  if (block != FP8BW_BLOCK_1x128 && block != FP8BW_BLOCK_128x128)
+    return fail(FP8BW_ERR_UNSUPPORTED, "unknown block kind %d", block);
+  if (transpose != 0 && transpose != 1) return fail(FP8BW_ERR_UNSUPPORTED, "transpose must be 0 or 1");
+  if (transpose && rows % 16) return fail(FP8BW_ERR_SHAPE, "transpose=1 needs rows %% 16 == 0 (rows=%lld)", (long long)rows);
+  int st = check_quant_common(x, rows, cols, ld_x, q, ld_q, transpose ? rows : cols);
+  if (st != FP8BW_OK) return st;
+  if (rows == 0 || cols == 0) return ok();
+  if (!recip) return fail(FP8BW_ERR_NULL, "recip must be non-null");
+  if (!aligned(recip, 4)) return fail(FP8BW_ERR_ALIGN, "recip must be 4-byte aligned");
+  // Scale grid [ni, nj] in (output row or row block, output column block).
+  int64_t ni, nj;
+  if (block == FP8BW_BLOCK_1x128) {
+    ni = transpose ? cols : rows;
+    nj = transpose ? cdiv(rows, 128) : cdiv(cols, 128);
+  } else {
+    ni = transpose ? cdiv(cols, 128) : cdiv(rows, 128);
+    nj = transpose ? cdiv(rows, 128) : cdiv(cols, 128);
+  }
+  if (!strides_injective(ni, nj, rs_row, rs_kb))
+    return fail(FP8BW_ERR_LAYOUT, "recip strides (%lld, %lld) alias or are negative for a %lldx%lld scale grid",
+                (long long)rs_row, (long long)rs_kb, (long long)ni, (long long)nj);
+  hipStream_t s = (hipStream_t)stream;
+  if (block == FP8BW_BLOCK_1x128 && !transpose) {
+    if (cdiv(cdiv(cols, 128), 4) > kMaxGridY) return fail(FP8BW_ERR_SHAPE, "too many column blocks");
+    return hip_status(fp8bw::launch_quant_1x128_rows(x, rows, cols, ld_x, q, ld_q, recip, rs_row, rs_kb, s),
+                      "fp8_blockwise_quant");
+  }
+  if (cdiv(rows, 128) > kMaxGridY) return fail(FP8BW_ERR_SHAPE, "too many row blocks");
+  if (block == FP8BW_BLOCK_1x128)
+    return hip_status(fp8bw::launch_quant_1x128_cols_t(x, rows, cols, ld_x, q, ld_q, recip, rs_row, rs_kb, s),
+                      "fp8_blockwise_quant");
+  return hip_status(fp8bw::launch_quant_128x128(x, rows, cols, ld_x, transpose, q, ld_q, recip, rs_row, rs_kb, s),
+                    "fp8_blockwise_quant");
+}
+
+FP8BW_API size_t fp8bw_tensorwise_quant_ws_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return 256;
+  return align_up((size_t)fp8bw::tensorwise_partials(rows, cols) * sizeof(float));
+}
+
+FP8BW_API int fp8_tensorwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   void* q, int64_t ld_q, float* recip, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  int st = check_quant_common(x, rows, cols, ld_x, q, ld_q, cols);
+  if (st != FP8BW_OK) return st;
+  if (!recip) return fail(FP8BW_ERR_NULL, "recip must be non-null");
+  if (!aligned(recip, 4)) return fail(FP8BW_ERR_ALIGN, "recip must be 4-byte aligned");
+  if (!ws || ws_bytes < fp8bw_tensorwise_quant_ws_bytes(rows, cols))
+    return fail(FP8BW_ERR_WORKSPACE, "workspace needs %zu bytes", fp8bw_tensorwise_quant_ws_bytes(rows, cols));
+  if (!aligned(ws, 4)) return fail(FP8BW_ERR_ALIGN, "ws must be 4-byte aligned");
+  const int64_t r = (rows == 0 || cols == 0) ? 0 : rows;
+  const int64_t c = (rows == 0 || cols == 0) ? 0 : cols;
+  return hip_status(fp8bw::launch_quant_tensorwise(x, r, c, ld_x, q, ld_q, recip, (float*)ws,
+                                                   (hipStream_t)stream),
+                    "fp8_tensorwise_quant");
+}
+
+// ---------------------------------------------------------------------------
+// GEMM.
+
+static int check_gemm_operands(const void* a, int64_t lda, const void* b, int64_t ldb,
+                               int64_t M, int64_t N, int64_t K, void* out, int64_t ldo,
+                               int out_dtype) {
+  if (out_dtype != FP8BW_OUT_BF16 && out_dtype != FP8BW_OUT_F32)
+    return fail(FP8BW_ERR_UNSUPPORTED, "unknown out_dtype %d", out_dtype);
+  if (M < 0 || N < 0 || K < 0)
+    return fail(FP8BW_ERR_SHAPE, "negative dimension (M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(FP8BW_ERR_SHAPE, "dimension too large");
+  if (M == 0 || N == 0) return FP8BW_OK;
+  if (!a || !b || !out) return fail(FP8BW_ERR_NULL, "a, b and out must be non-null");
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16))
+    return fail(FP8BW_ERR_ALIGN, "a, b and out must be 16-byte aligned");
+  if (lda < K || ldb < K || lda % 16 || ldb % 16)
+    return fail(FP8BW_ERR_LAYOUT, "lda/ldb (%lld/%lld) must be >= K and multiples of 16", (long long)lda, (long long)ldb);
+  if (ldo < N) return fail(FP8BW_ERR_LAYOUT, "ldo=%lld must be >= N", (long long)ldo);
+  return FP8BW_OK;
+}
+
+static int gemm_blockwise_impl(const void* a, int64_t lda, const float* ra, int64_t ra_s_row,
+                               int64_t ra_s_kb, const void* b, int64_t ldb, const float* rb,
+                               int64_t rb_s_row, int64_t rb_s_kb, int b_block, int64_t M,
+                               int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype,
+                               int config, int splits, void* ws, size_t ws_bytes, void* stream) {
+  if (b_block != FP8BW_BLOCK_1x128 && b_block != FP8BW_BLOCK_128x128)
+    return fail(FP8BW_ERR_UNSUPPORTED, "unknown b_block %d", b_block);
+  int st = check_gemm_operands(a, lda, b, ldb, M, N, K, out, ldo, out_dtype);
+  if (st != FP8BW_OK) return st;
+  if (K % 128) return fail(FP8BW_ERR_SHAPE, "blockwise GEMM needs K %% 128 == 0 (K=%lld)", (long long)K);
+  if (M == 0 || N == 0) return ok();
+  const int64_t kb = K / 128;
+  if (kb > 0) {
+    if (!ra || !rb) return fail(FP8BW_ERR_NULL, "ra and rb must be non-null");
+    if (!aligned(ra, 4) || !aligned(rb, 4)) return fail(FP8BW_ERR_ALIGN, "ra/rb must be 4-byte aligned");
+    // Strides of size-1 dimensions are never used and may be anything.
+    if ((M > 1 && ra_s_row != 1) || (kb > 1 && ra_s_kb < M))
+      return fail(FP8BW_ERR_LAYOUT, "ra must be column-major: ra_s_row == 1 and ra_s_kb >= M");
+    if (b_block == FP8BW_BLOCK_1x128) {
+      if ((N > 1 && rb_s_row != 1) || (kb > 1 && rb_s_kb < N))
+        return fail(FP8BW_ERR_LAYOUT, "1x128 rb must be column-major: rb_s_row == 1 and rb_s_kb >= N");
+    } else if (!strides_injective(cdiv(N, 128), kb, rb_s_row, rb_s_kb)) {
+      return fail(FP8BW_ERR_LAYOUT, "rb strides (%lld, %lld) alias or are negative", (long long)rb_s_row, (long long)rb_s_kb);
+    }
+  }
+  fp8bw::GemmProblem p;
+  p.a = a; p.lda = lda; p.b = b; p.ldb = ldb;
+  p.ra = ra; p.ra_s_row = ra_s_row; p.ra_s_kb = ra_s_kb;
+  p.rb = rb; p.rb_s_row = rb_s_row; p.rb_s_kb = rb_s_kb;
+  p.out = out; p.ldo = ldo; p.M = M; p.N = N; p.K = K;
+  p.mode = b_block == FP8BW_BLOCK_128x128 ? fp8bw::kBlockB128 : fp8bw::kBlockB1x128;
+  p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
+  int cfg = 0, sp = 1;
+  fp8bw::gemm_choose(p, &cfg, &sp);
+  if (config >= 0) {
+    if (!fp8bw::gemm_config_ok(p, config)) return fail(FP8BW_ERR_UNSUPPORTED, "config %d not available", config);
+    cfg = config;
+  }
+  if (splits > 0) sp = splits;
+  if (sp > kMaxGridY || (kb > 0 && sp > kb) || (kb == 0 && sp > 1))
+    return fail(FP8BW_ERR_SHAPE, "splits=%d must be <= the number of K blocks (%lld)", sp, (long long)kb);
+  const size_t need = fp8bw::gemm_ws_bytes(M, N, sp);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return fail(FP8BW_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+    if (!aligned(ws, 16)) return fail(FP8BW_ERR_ALIGN, "ws must be 16-byte aligned");
+  }
+  return hip_status(fp8bw::launch_gemm(p, cfg, sp, ws, (hipStream_t)stream), "fp8_scaled_gemm_blockwise");
+}
+
+static fp8bw::GemmProblem size_only_problem(int64_t M, int64_t N, int64_t K) {
+  fp8bw::GemmProblem p = {};
+  p.M = M; p.N = N; p.K = K;
+  p.mode = fp8bw::kBlockB128;
+  return p;
+}
+
+FP8BW_API size_t fp8bw_gemm_blockwise_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  fp8bw::GemmProblem p = size_only_problem(M, N, K);
+  int cfg = 0, sp = 1;
+  fp8bw::gemm_choose(p, &cfg, &sp);
+  return fp8bw::gemm_ws_bytes(M, N, sp);
+}
+
+FP8BW_API int fp8bw_gemm_num_configs(void) { return fp8bw::gemm_num_configs(); }
+
+FP8BW_API size_t fp8bw_gemm_ws_bytes_for_split(int64_t M, int64_t N, int splits) {
+  if (M <= 0 || N <= 0) return 0;
+  return fp8bw::gemm_ws_bytes(M, N, splits);
+}
+
+FP8BW_API int fp8_scaled_gemm_blockwise(const void* a, int64_t lda, const float* ra,
+                                        int64_t ra_s_row, int64_t ra_s_kb, const void* b,
+                                        int64_t ldb, const float* rb, int64_t rb_s_row,
+                                        int64_t rb_s_kb, int b_block, int64_t M, int64_t N,
+                                        int64_t K, void* out, int64_t ldo, int out_dtype,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  return gemm_blockwise_impl(a, lda, ra, ra_s_row, ra_s_kb, b, ldb, rb, rb_s_row, rb_s_kb, b_block,
+                             M, N, K, out, ldo, out_dtype, -1, 0, ws, ws_bytes, stream);
+}
+
+FP8BW_API int fp8_scaled_gemm_blockwise_cfg(const void* a, int64_t lda, const float* ra,
+                                            int64_t ra_s_row, int64_t ra_s_kb, const void* b,
+                                            int64_t ldb, const float* rb, int64_t rb_s_row,
+                                            int64_t rb_s_kb, int b_block, int64_t M, int64_t N,
+                                            int64_t K, void* out, int64_t ldo, int out_dtype,
+                                            int config, int splits, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  if (config < -1 || config >= fp8bw::gemm_num_configs())
+    return fail(FP8BW_ERR_UNSUPPORTED, "config %d out of range", config);
+  if (splits < 0) return fail(FP8BW_ERR_SHAPE, "splits must be >= 0");
+  return gemm_blockwise_impl(a, lda, ra, ra_s_row, ra_s_kb, b, ldb, rb, rb_s_row, rb_s_kb, b_block,
+                             M, N, K, out, ldo, out_dtype, config, splits, ws, ws_bytes, stream);
+}
+
+FP8BW_API int fp8_scaled_gemm_tensorwise(const void* a, int64_t lda, const float* ra,
+                                         const void* b, int64_t ldb, const float* rb, int64_t M,
+                                         int64_t N, int64_t K, void* out, int64_t ldo,
+                                         int out_dtype, void* stream) {
+  int st = check_gemm_operands(a, lda, b, ldb, M, N, K, out, ldo, out_dtype);
+  if (st != FP8BW_OK) return st;
+  if (K % 16) return fail(FP8BW_ERR_SHAPE, "tensorwise GEMM needs K %% 16 == 0 (K=%lld)", (long long)K);
+  if (M == 0 || N == 0) return ok();
+  if (!ra || !rb) return fail(FP8BW_ERR_NULL, "ra and rb must be non-null");
+  if (!aligned(ra, 4) || !aligned(rb, 4)) return fail(FP8BW_ERR_ALIGN, "ra/rb must be 4-byte aligned");
+  fp8bw::GemmProblem p = {};
+  p.a = a; p.lda = lda; p.b = b; p.ldb = ldb;
+  p.ra = ra; p.rb = rb;
+  p.out = out; p.ldo = ldo; p.M = M; p.N = N; p.K = K;
+  p.mode = fp8bw::kTensorwise;
+  p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
+  int cfg = 0, sp = 1;
+  fp8bw::gemm_choose(p, &cfg, &sp);
+  return hip_status(fp8bw::launch_gemm(p, cfg, 1, nullptr, (hipStream_t)stream), "fp8_scaled_gemm_tensorwise");
+}
+
+// ---------------------------------------------------------------------------
+// Linear wrapper.  Workspace layout (each region 256-byte aligned):
+//   [A codes][B codes][A recip][B recip][GEMM split-K partials]
+
+namespace {
+
+struct LinearLayout {
+  int64_t gm, gn, gk;          // GEMM shape
+  size_t a_codes, b_codes, a_recip, b_recip, gemm_ws, total;
+};
+
+LinearLayout linear_layout(int64_t M, int64_t N, int64_t K, int which) {
+  LinearLayout L = {};
+  if (which == 0) { L.gm = M; L.gn = N; L.gk = K; }
+  else if (which == 1) { L.gm = M; L.gn = K; L.gk = N; }
+  else { L.gm = N; L.gn = K; L.gk = M; }
+  const int64_t kb = cdiv(L.gk, 128);
+  size_t off = 0;
+  L.a_codes = off; off += align_up((size_t)(L.gm * L.gk));
+  L.b_codes = off; off += align_up((size_t)(L.gn * L.gk));
+  L.a_recip = off; off += align_up((size_t)(L.gm * kb) * 4);
+  // 128x128 B scales need cdiv(gn,128)*kb; 1x128 (wgrad) need gn*kb.
+  L.b_recip = off; off += align_up((size_t)((which == 2 ? L.gn : cdiv(L.gn, 128)) * kb) * 4);
+  L.gemm_ws = off; off += align_up(fp8bw_gemm_blockwise_ws_bytes(L.gm, L.gn, L.gk));
+  L.total = off;
+  return L;
+}
+
+int check_linear(const void* p0, const void* p1, void* out, int64_t M, int64_t N, int64_t K,
+                 void* ws, size_t ws_bytes, int which) {
+  if (M < 0 || N < 0 || K < 0) return fail(FP8BW_ERR_SHAPE, "negative dimension");
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(FP8BW_ERR_SHAPE, "dimension too large");
+  if (M % 16 || N % 16 || K % 16) return fail(FP8BW_ERR_SHAPE, "M, N, K must be multiples of 16");
+  const int64_t contraction = which == 0 ? K : which == 1 ? N : M;
+  if (contraction % 128)
+    return fail(FP8BW_ERR_SHAPE, "the contraction dimension (%lld) must be a multiple of 128", (long long)contraction);
+  if (M == 0 || N == 0 || K == 0) return FP8BW_OK;
+  if (!p0 || !p1 || !out) return fail(FP8BW_ERR_NULL, "inputs and output must be non-null");
+  if (!aligned(p0, 16) || !aligned(p1, 16) || !aligned(out, 16))
+    return fail(FP8BW_ERR_ALIGN, "tensors must be 16-byte aligned");
+  const LinearLayout L = linear_layout(M, N, K, which);
+  if (!ws || ws_bytes < L.total) return fail(FP8BW_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
+  if (!aligned(ws, 256)) return fail(FP8BW_ERR_ALIGN, "ws must be 256-byte aligned");
+  return FP8BW_OK;
+}
+
+}  // namespace
+
+FP8BW_API size_t fp8bw_linear_ws_bytes(int64_t M, int64_t N, int64_t K, int which) {
+  if (which < 0 || which > 2 || M <= 0 || N <= 0 || K <= 0) return 0;
+  return linear_layout(M, N, K, which).total;
+}
+
+static int zero_output(void* out, int64_t rows, int64_t cols, void* stream) {
+  // Empty contraction: the product is all zeros (a fill kernel, not a memset
+  // node, so the call stays safe to capture into a graph).
+  return hip_status(fp8bw::launch_zero_bf16(out, rows, cols, (hipStream_t)stream), "zero output");
+}
+
+FP8BW_API int fp8_linear_fwd(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                             int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear(x, w, y, M, N, K, ws, ws_bytes, 0);
+  if (st != FP8BW_OK) return st;
+  if (M == 0 || N == 0) return ok();
+  if (K == 0) return zero_output(y, M, N, stream);
+  const LinearLayout L = linear_layout(M, N, K, 0);
+  uint8_t* base = (uint8_t*)ws;
+  const int64_t kb = K / 128, nb = cdiv(N, 128);
+  uint8_t* xq = base + L.a_codes;
+  uint8_t* wq = base + L.b_codes;
+  float* xr = (float*)(base + L.a_recip);
+  float* wr = (float*)(base + L.b_recip);
+  if ((st = fp8_blockwise_quant(x, M, K, K, FP8BW_BLOCK_1x128, 0, xq, K, xr, 1, M, stream))) return st;
+  if ((st = fp8_blockwise_quant(w, N, K, K, FP8BW_BLOCK_128x128, 0, wq, K, wr, 1, nb, stream))) return st;
+  (void)kb;
+  return fp8_scaled_gemm_blockwise(xq, K, xr, 1, M, wq, K, wr, 1, nb, FP8BW_BLOCK_128x128, M, N, K,
+                                   y, N, FP8BW_OUT_BF16, base + L.gemm_ws, ws_bytes - L.gemm_ws, stream);
+}
+
+FP8BW_API int fp8_linear_dgrad(const void* dy, const void* w, void* dx, int64_t M, int64_t N,
+                               int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear(dy, w, dx, M, N, K, ws, ws_bytes, 1);
+  if (st != FP8BW_OK) return st;
+  if (M == 0 || K == 0) return ok();
+  if (N == 0) return zero_output(dx, M, K, stream);
+  const LinearLayout L = linear_layout(M, N, K, 1);
+  uint8_t* base = (uint8_t*)ws;
+  const int64_t kbo = cdiv(K, 128);
+  uint8_t* dyq = base + L.a_codes;
+  uint8_t* wtq = base + L.b_codes;
+  float* dyr = (float*)(base + L.a_recip);
+  float* wtr = (float*)(base + L.b_recip);
+  // dY: 1x128 along N, column-major scales dyr[m + nb*M].
+  if ((st = fp8_blockwise_quant(dy, M, N, N, FP8BW_BLOCK_1x128, 0, dyq, N, dyr, 1, M, stream))) return st;
+  // W^T [K, N] codes; scales indexed (K block, N block): wtr[kbo_i + nb*kbo].
+  if ((st = fp8_blockwise_quant(w, N, K, K, FP8BW_BLOCK_128x128, 1, wtq, N, wtr, 1, kbo, stream))) return st;
+  return fp8_scaled_gemm_blockwise(dyq, N, dyr, 1, M, wtq, N, wtr, 1, kbo, FP8BW_BLOCK_128x128, M, K, N,
+                                   dx, K, FP8BW_OUT_BF16, base + L.gemm_ws, ws_bytes - L.gemm_ws, stream);
+}
+
+FP8BW_API int fp8_linear_wgrad(const void* dy, const void* x, void* dw, int64_t M, int64_t N,
+                               int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_linear(dy, x, dw, M, N, K, ws, ws_bytes, 2);
+  if (st != FP8BW_OK) return st;
+  if (N == 0 || K == 0) return ok();
+  if (M == 0) return zero_output(dw, N, K, stream);
+  const LinearLayout L = linear_layout(M, N, K, 2);
+  uint8_t* base = (uint8_t*)ws;
+  uint8_t* dytq = base + L.a_codes;
+  uint8_t* xtq = base + L.b_codes;
+  float* dytr = (float*)(base + L.a_recip);
+  float* xtr = (float*)(base + L.b_recip);
+  // dY^T [N, M] with 1x128 blocks along M: dytr[n + mb*N].
+  if ((st = fp8_blockwise_quant(dy, M, N, N, FP8BW_BLOCK_1x128, 1, dytq, M, dytr, 1, N, stream))) return st;
+  // X^T [K, M]: xtr[k + mb*K].
+  if ((st = fp8_blockwise_quant(x, M, K, K, FP8BW_BLOCK_1x128, 1, xtq, M, xtr, 1, K, stream))) return st;
+  return fp8_scaled_gemm_blockwise(dytq, M, dytr, 1, N, xtq, M, xtr, 1, K, FP8BW_BLOCK_1x128, N, K, M,
+                                   dw, K, FP8BW_OUT_BF16, base + L.gemm_ws, ws_bytes - L.gemm_ws, stream);
+}

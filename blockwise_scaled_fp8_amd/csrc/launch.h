@@ -1,0 +1,60 @@
+// Internal host-side launchers shared by the C ABI (api.cpp) and the kernel
+// translation units.  Arguments are validated by the caller (api.cpp); the
+// launchers only size grids and enqueue on `stream`.  Each returns the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fp8bw {
+
+// ---- quantization (quant.hip) ----
+// 1x128 blocks along columns: q[r, c], recip[r*rs_row + kb*rs_kb].
+hipError_t launch_quant_1x128_rows(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   void* q, int64_t ld_q, float* recip, int64_t rs_row,
+                                   int64_t rs_kb, hipStream_t stream);
+// 128x128 tiles; transpose=1 writes q = x^T [cols, rows] and indexes recip by
+// (output row block, output column block).
+hipError_t launch_quant_128x128(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                int transpose, void* q, int64_t ld_q, float* recip,
+                                int64_t rs_row, int64_t rs_kb, hipStream_t stream);
+// 1x128 blocks running down the rows; output transposed q = x^T [cols, rows],
+// recip[c*rs_row + mb*rs_kb].
+hipError_t launch_quant_1x128_cols_t(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                     void* q, int64_t ld_q, float* recip, int64_t rs_row,
+                                     int64_t rs_kb, hipStream_t stream);
+// Per-tensor: partial amax into ws (n_partials floats), then quantize.
+int tensorwise_partials(int64_t rows, int64_t cols);
+hipError_t launch_quant_tensorwise(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   void* q, int64_t ld_q, float* recip, float* ws,
+                                   hipStream_t stream);
+
+// ---- GEMM (gemm.hip) ----
+enum ScaleMode { kBlockB128 = 0, kBlockB1x128 = 1, kTensorwise = 2 };
+enum OutKind { kOutBf16 = 0, kOutF32 = 1 };
+
+struct GemmProblem {
+  const void* a; int64_t lda;
+  const void* b; int64_t ldb;
+  const float* ra; int64_t ra_s_row, ra_s_kb;
+  const float* rb; int64_t rb_s_row, rb_s_kb;
+  void* out; int64_t ldo;
+  int64_t M, N, K;
+  int mode;       // ScaleMode
+  int out_kind;   // OutKind
+};
+
+// Tile configurations; the table lives in gemm.hip.
+int gemm_num_configs();
+// Heuristic choice of (config, split) for a problem.
+void gemm_choose(const GemmProblem& p, int* config, int* splits);
+// Whether config `cfg` accepts this problem (mode support).
+bool gemm_config_ok(const GemmProblem& p, int cfg);
+// Workspace bytes for a split count (fp32 partials [splits, M, N]).
+size_t gemm_ws_bytes(int64_t M, int64_t N, int splits);
+hipError_t launch_gemm(const GemmProblem& p, int cfg, int splits, void* ws, hipStream_t stream);
+// Fill a contiguous bf16 [rows, cols] matrix with +0.
+hipError_t launch_zero_bf16(void* out, int64_t rows, int64_t cols, hipStream_t stream);
+
+}  // namespace fp8bw

@@ -1,0 +1,212 @@
+"""Thin torch-facing binding of the C ABI: the same entry-point names as
+include/fp8bw.h.  Each function only checks tensor placement, allocates its
+outputs with torch (device memory is plumbing), passes raw pointers, sizes and
+the current HIP stream, and raises FP8BWError on a non-OK status.  Every step
+of the computation runs in the HIP kernels of libfp8bw.so."""
+
+import torch
+
+from ._lib import check, load_library
+
+BLOCKS = {"1x128": 0, "128x128": 1}
+OUT_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not (isinstance(t, torch.Tensor) and t.is_cuda):
+            raise ValueError("fp8bw ops take CUDA (HIP) tensors")
+
+
+def _rowmajor(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+
+
+def _cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def scale_grid(rows, cols, block, transpose):
+    """Logical shape (ni, nj) of the reciprocal-scale tensor."""
+    if block == "1x128":
+        return (cols, _cdiv(rows, 128)) if transpose else (rows, _cdiv(cols, 128))
+    return (_cdiv(cols, 128), _cdiv(rows, 128)) if transpose else (_cdiv(rows, 128), _cdiv(cols, 128))
+
+
+def colmajor_empty(ni, nj, device):
+    """fp32 [ni, nj] with column-major strides (1, ni)."""
+    return torch.empty((nj, max(ni, 1)), dtype=torch.float32, device=device)[:, :ni].t()
+
+
+def _check_codes(a, b, K):
+    for t in (a, b):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError("GEMM operands are E4M3 codes (uint8 or float8_e4m3fn)")
+    if b.shape[1] != K:
+        raise ValueError(f"b has K={b.shape[1]}, a has K={K}")
+
+
+def _check_shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def fp8_blockwise_quant(x, block="1x128", transpose=False, q=None, recip=None):
+    """Quantize bf16 x[rows, cols] to E4M3 codes with per-block reciprocal scales.
+
+    Returns (q, recip): q uint8 [rows, cols] (or [cols, rows] with transpose),
+    recip fp32 [ni, nj] (column-major unless a tensor is passed in)."""
+    lib = load_library()
+    _need_cuda(x)
+    _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    rows, cols = x.shape
+    qshape = (cols, rows) if transpose else (rows, cols)
+    if q is None:
+        q = torch.empty(qshape, dtype=torch.uint8, device=x.device)
+    _check_shape(q, qshape, "q")
+    ni, nj = scale_grid(rows, cols, block, transpose)
+    if recip is None:
+        recip = colmajor_empty(ni, nj, x.device)
+    _check_shape(recip, (ni, nj), "recip")
+    check(lib.fp8_blockwise_quant(x.data_ptr(), rows, cols, x.stride(0), BLOCKS[block],
+                                  int(bool(transpose)), q.data_ptr(), q.stride(0),
+                                  recip.data_ptr(), recip.stride(0), recip.stride(1), _stream(x)))
+    return q, recip
+
+
+def fp8_tensorwise_quant(x, q=None, recip=None):
+    """Per-tensor quantization: (q uint8 like x, recip fp32 [1] on device)."""
+    lib = load_library()
+    _need_cuda(x)
+    _rowmajor(x, "x")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if recip is None:
+        recip = torch.empty(1, dtype=torch.float32, device=x.device)
+    nws = lib.fp8bw_tensorwise_quant_ws_bytes(rows, cols)
+    ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
+    check(lib.fp8_tensorwise_quant(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0),
+                                   recip.data_ptr(), ws.data_ptr(), nws, _stream(x)))
+    return q, recip
+
+
+def fp8_scaled_gemm_blockwise(a, ra, b, rb, b_block="128x128", out_dtype=torch.bfloat16,
+                              out=None, config=None, splits=None):
+    """out[M, N] = blockwise-scaled A . B^T (see include/fp8bw.h).
+
+    a uint8 [M, K], ra fp32 [M, K/128] (column-major), b uint8 [N, K], rb fp32
+    [N/128 or N, K/128].  config/splits force a tile configuration / split-K
+    count (None = built-in choice)."""
+    lib = load_library()
+    _need_cuda(a, b, ra, rb)
+    _rowmajor(a, "a")
+    _rowmajor(b, "b")
+    M, K = a.shape
+    N = b.shape[0]
+    _check_codes(a, b, K)
+    kb = _cdiv(K, 128)
+    _check_shape(ra, (M, kb), "ra")
+    _check_shape(rb, (N if b_block == "1x128" else _cdiv(N, 128), kb), "rb")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check_shape(out, (M, N), "out")
+    args = (a.data_ptr(), a.stride(0), ra.data_ptr(), ra.stride(0), ra.stride(1),
+            b.data_ptr(), b.stride(0), rb.data_ptr(), rb.stride(0), rb.stride(1),
+            BLOCKS[b_block], M, N, K, out.data_ptr(), out.stride(0), OUT_DTYPES[out.dtype])
+    if config is None and splits is None:
+        nws = lib.fp8bw_gemm_blockwise_ws_bytes(M, N, K)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=a.device)
+        check(lib.fp8_scaled_gemm_blockwise(*args, ws.data_ptr(), nws, _stream(a)))
+    else:
+        s = 0 if splits is None else int(splits)
+        if s > 0:
+            nws = lib.fp8bw_gemm_ws_bytes_for_split(M, N, s)
+        else:
+            nws = lib.fp8bw_gemm_blockwise_ws_bytes(M, N, K)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=a.device)
+        check(lib.fp8_scaled_gemm_blockwise_cfg(*args, -1 if config is None else int(config), s,
+                                                ws.data_ptr(), nws, _stream(a)))
+    return out
+
+
+def fp8bw_gemm_num_configs():
+    return load_library().fp8bw_gemm_num_configs()
+
+
+def fp8_scaled_gemm_tensorwise(a, ra, b, rb, out_dtype=torch.bfloat16, out=None):
+    """out[M, N] = (A . B^T) * ra * rb with one-element device scales."""
+    lib = load_library()
+    _need_cuda(a, b, ra, rb)
+    _rowmajor(a, "a")
+    _rowmajor(b, "b")
+    M, K = a.shape
+    N = b.shape[0]
+    _check_codes(a, b, K)
+    if ra.numel() != 1 or rb.numel() != 1:
+        raise ValueError("tensorwise scales are one-element tensors")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check_shape(out, (M, N), "out")
+    check(lib.fp8_scaled_gemm_tensorwise(a.data_ptr(), a.stride(0), ra.data_ptr(), b.data_ptr(),
+                                         b.stride(0), rb.data_ptr(), M, N, K, out.data_ptr(),
+                                         out.stride(0), OUT_DTYPES[out.dtype], _stream(a)))
+    return out
+
+
+def linear_workspace(M, N, K, which, device):
+    n = load_library().fp8bw_linear_ws_bytes(M, N, K, which)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _linear(name, which, p0, p1, out_shape, M, N, K, ws):
+    lib = load_library()
+    _need_cuda(p0, p1)
+    if not (p0.is_contiguous() and p1.is_contiguous()):
+        raise ValueError("linear inputs must be contiguous")
+    out = torch.empty(out_shape, dtype=torch.bfloat16, device=p0.device)
+    if ws is None:
+        ws = linear_workspace(M, N, K, which, p0.device)
+    check(getattr(lib, name)(p0.data_ptr(), p1.data_ptr(), out.data_ptr(), M, N, K,
+                             ws.data_ptr(), ws.numel(), _stream(p0)))
+    return out
+
+
+def _bf16_2d(*ts):
+    for t in ts:
+        if t.dim() != 2 or t.dtype != torch.bfloat16:
+            raise ValueError("linear inputs are 2-D bf16 tensors")
+
+
+def fp8_linear_fwd(x, w, ws=None):
+    """Y[M, N] = X . W^T (X 1x128, W 128x128), bf16."""
+    _bf16_2d(x, w)
+    M, K = x.shape
+    N = w.shape[0]
+    _check_shape(w, (N, K), "w")
+    return _linear("fp8_linear_fwd", 0, x, w, (M, N), M, N, K, ws)
+
+
+def fp8_linear_dgrad(dy, w, ws=None):
+    """dX[M, K] = dY . W (dY 1x128, W^T 128x128), bf16."""
+    _bf16_2d(dy, w)
+    M, N = dy.shape
+    K = w.shape[1]
+    _check_shape(w, (N, K), "w")
+    return _linear("fp8_linear_dgrad", 1, dy, w, (M, K), M, N, K, ws)
+
+
+def fp8_linear_wgrad(dy, x, ws=None):
+    """dW[N, K] = dY^T . X (1x128 x 1x128 along M), bf16."""
+    _bf16_2d(dy, x)
+    M, N = dy.shape
+    K = x.shape[1]
+    _check_shape(x, (M, K), "x")
+    return _linear("fp8_linear_wgrad", 2, dy, x, (N, K), M, N, K, ws)

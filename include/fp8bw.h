@@ -1,0 +1,201 @@
+/*
+ * fp8bw.h -- C ABI of libfp8bw.so: blockwise- and tensorwise-scaled FP8
+ * (OCP E4M3) quantization and GEMM for AMD MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [REPRO]   pytorch/ao PR "add repro for blockwise _scaled_mm
+ *             investigation" -- What Changed; Findings So Far; review
+ *             comments (the 1x128 x 128x128 and 1x128 x 1x128 recipes).
+ *   [INTEG]   pytorch/ao PR "integrate torch._scaled_mm into
+ *             Float8BlockwiseLinear and add bench script" -- Summary
+ *             (reciprocal scales, column-major scale layout); Benchmarks
+ *             (linear forward + backward at M16640 N5120 K8192).
+ *   [GENERIC] pytorch/ao PR "add more generic kernel for fp8 blockwise
+ *             scaling" -- Performance table (1x128 and 128x128 blocks).
+ *   [AITER]   ROCm/aiter issue "Does gemm_a8w8 support per-tensor quant?"
+ *             -- Steps to Reproduce (per-tensor quant, out = x @ w.T,
+ *             dequant reference x_q.float() * x_scale).
+ *   [INDUCT]  pytorch/pytorch inductor FP8 tensorwise issue -- Describe the
+ *             bug (16x32x32 fp32-out tensorwise case).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers marked "device" are HIP device pointers; the library never
+ *    allocates, frees or copies device memory and never synchronizes the
+ *    host.  Scratch comes from a caller-owned workspace sized by the
+ *    matching *_ws_bytes query.  The caller owns every buffer.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  All work
+ *    is enqueued on it in order; the call returns after enqueueing.
+ *  - bf16 tensors are raw 16-bit bf16 bit patterns; FP8 tensors are OCP
+ *    E4M3 ("e4m3fn") codes, one byte each; scales are fp32.
+ *  - Matrices are row-major with a leading dimension `ld*` in elements.
+ *    Every matrix pointer must be 16-byte aligned, bf16 input leading
+ *    dimensions a multiple of 8 and FP8 leading dimensions a multiple of 16
+ *    (GEMM output leading dimensions only need ldo >= N).  The stride of a
+ *    dimension of size 1 is ignored.
+ *  - A *reciprocal scale* ("recip") is the dequantization multiplier: the
+ *    quantizer computes s = 448 / max(amax, 1e-12) per block, stores
+ *    codes = satRNE_e4m3(x * s) and recip = 1 / s (both fp32 IEEE ops),
+ *    so x ~= e4m3_value(code) * recip ([INTEG] Summary; [AITER]).
+ *  - Validation runs on the host before any HIP call.  A rejected call
+ *    enqueues nothing and returns a status != FP8BW_OK;
+ *    fp8bw_last_error() gives a message for the calling thread.  A launch
+ *    failure returns FP8BW_ERR_HIP.  No exception crosses the ABI and the
+ *    library prints nothing.
+ *  - Zero-sized problems (rows == 0, cols == 0, M == 0 or N == 0) succeed
+ *    and enqueue nothing (the tensorwise quantizer still writes its recip).
+ *  - Inputs must be finite; outputs must not alias inputs.  Results for
+ *    non-finite inputs are unspecified.
+ */
+#ifndef FP8BW_H
+#define FP8BW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8BW_OK = 0,
+  FP8BW_ERR_NULL = 1,        /* a required pointer is NULL */
+  FP8BW_ERR_SHAPE = 2,       /* negative or unsupported dimension */
+  FP8BW_ERR_LAYOUT = 3,      /* leading dimension / scale stride not allowed */
+  FP8BW_ERR_ALIGN = 4,       /* pointer or leading dimension misaligned */
+  FP8BW_ERR_UNSUPPORTED = 5, /* unknown enum value or config */
+  FP8BW_ERR_WORKSPACE = 6,   /* workspace NULL or too small */
+  FP8BW_ERR_HIP = 7          /* a HIP launch failed */
+} fp8bw_status;
+
+typedef enum { FP8BW_BLOCK_1x128 = 0, FP8BW_BLOCK_128x128 = 1 } fp8bw_block;
+typedef enum { FP8BW_OUT_BF16 = 0, FP8BW_OUT_F32 = 1 } fp8bw_out;
+
+/* Version of this ABI (incremented on incompatible change). */
+int fp8bw_abi_version(void);
+/* Static string for a status code. */
+const char* fp8bw_status_str(int status);
+/* Message for the last rejected call on this thread ("" if none). */
+const char* fp8bw_last_error(void);
+
+/*
+ * fp8_blockwise_quant -- dynamic E4M3 quantization with per-block amax
+ * scales ([GENERIC] Performance table: block_shape (1,128) and (128,128);
+ * [INTEG] Summary: reciprocal scales written by the quantizer itself).
+ *
+ *   x      device bf16 [rows, cols], leading dim ld_x.
+ *   block  FP8BW_BLOCK_1x128: one scale per row per 128 columns
+ *          (transpose=0), or per column per 128 rows (transpose=1: the
+ *          wgrad operands dY^T, X^T).
+ *          FP8BW_BLOCK_128x128: one scale per 128x128 tile (weights);
+ *          transpose=1 writes W^T codes for the dgrad GEMM.  A tile's amax
+ *          is orientation-independent, so these codes are exactly the
+ *          transpose of the transpose=0 codes.
+ *   q      device E4M3 output.  transpose=0: q[rows, cols] (ld_q >= cols).
+ *          transpose=1: q = x^T [cols, rows] (ld_q >= rows).
+ *   recip  device fp32 reciprocal scales, indexed by (output row or output
+ *          row block i, output column block j) at recip[i*rs_row + j*rs_kb]:
+ *            1x128,   transpose=0: i = row r, j = r's 128-column block
+ *            1x128,   transpose=1: i = column c (output row), j = 128-row block
+ *            128x128, transpose=0: i = 128-row block, j = 128-column block
+ *            128x128, transpose=1: i = 128-column block, j = 128-row block
+ *          Column-major ([INTEG] Summary) is rs_row = 1, rs_kb = number of
+ *          i indices; any non-negative strides are accepted.
+ *   Blocks at a ragged edge take their amax over the valid elements only.
+ *   Requires cols % 16 == 0, and rows % 16 == 0 when transpose=1.
+ */
+int fp8_blockwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int block,
+                        int transpose, void* q, int64_t ld_q, float* recip, int64_t rs_row,
+                        int64_t rs_kb, void* stream);
+
+/*
+ * fp8_tensorwise_quant -- one scale for the whole tensor ([AITER]
+ * per_tensor_quant: the scale returned is the dequant multiplier).
+ *   x [rows, cols] bf16 (ld_x), q [rows, cols] E4M3 (ld_q), recip: one
+ *   device fp32.  ws: device scratch of fp8bw_tensorwise_quant_ws_bytes().
+ *   Two launches (partial amax, then quantize); deterministic.
+ *   Requires cols % 16 == 0.
+ */
+size_t fp8bw_tensorwise_quant_ws_bytes(int64_t rows, int64_t cols);
+int fp8_tensorwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* q,
+                         int64_t ld_q, float* recip, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp8_scaled_gemm_blockwise -- out[M, N] = sum_kb ra[m, kb] * rb[beta(n), kb]
+ *                              * sum_{k in block kb} a[m, k] * b[n, k]
+ * ([REPRO] What Changed: the blockwise GEMM on the same codes and
+ * reciprocal scales as the dequantized matmul; out = A . B^T as F.linear).
+ *
+ *   a   device E4M3 [M, K], lda; ra: 1x128 scales of A, ra[m + kb*ra_s_kb]
+ *       (column-major; ra_s_kb >= M).
+ *   b   device E4M3 [N, K], ldb.  b_block selects rb's meaning:
+ *         FP8BW_BLOCK_128x128: rb[(n/128)*rb_s_row + kb*rb_s_kb]  (fwd, dgrad)
+ *         FP8BW_BLOCK_1x128:   rb[n + kb*rb_s_kb], rb_s_row must be 1 (wgrad)
+ *   out device [M, N] bf16 (RNE from the fp32 accumulator) or fp32, ldo.
+ *   K % 128 == 0 (K blocks may number anything, e.g. 1001 or 1002).
+ *   Each K block is accumulated in fp32 by the matrix cores and rescaled in
+ *   fp32 before it is added to the running sum.
+ *   ws: device scratch for split-K partials; size from
+ *   fp8bw_gemm_blockwise_ws_bytes(M, N, K) (may be 0 -> ws may be NULL).
+ */
+size_t fp8bw_gemm_blockwise_ws_bytes(int64_t M, int64_t N, int64_t K);
+int fp8_scaled_gemm_blockwise(const void* a, int64_t lda, const float* ra, int64_t ra_s_row,
+                              int64_t ra_s_kb, const void* b, int64_t ldb, const float* rb,
+                              int64_t rb_s_row, int64_t rb_s_kb, int b_block, int64_t M,
+                              int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Same as fp8_scaled_gemm_blockwise with an explicit tile configuration
+ * (0 .. fp8bw_gemm_num_configs()-1, or -1 for the built-in choice) and
+ * split-K count (>= 1, or 0 for the built-in choice).  Every configuration
+ * computes the same result up to fp32 rounding order; this entry point
+ * lets tests force each one (a kernel variant can be wrong where the
+ * others are right: [INDUCT] Describe the bug).  Workspace for an explicit
+ * split s is fp8bw_gemm_ws_bytes_for_split(M, N, s).
+ */
+int fp8bw_gemm_num_configs(void);
+size_t fp8bw_gemm_ws_bytes_for_split(int64_t M, int64_t N, int splits);
+int fp8_scaled_gemm_blockwise_cfg(const void* a, int64_t lda, const float* ra, int64_t ra_s_row,
+                                  int64_t ra_s_kb, const void* b, int64_t ldb, const float* rb,
+                                  int64_t rb_s_row, int64_t rb_s_kb, int b_block, int64_t M,
+                                  int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype,
+                                  int config, int splits, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/*
+ * fp8_scaled_gemm_tensorwise -- out[M, N] = (sum_k a[m, k] * b[n, k]) * ra * rb
+ * ([AITER]: per-tensor scales, out = x @ w.T; [INDUCT]: fp32 output).
+ *   ra, rb: one device fp32 each (dequant multipliers).
+ *   K % 16 == 0 (K need not be a multiple of 128).  No workspace.
+ */
+int fp8_scaled_gemm_tensorwise(const void* a, int64_t lda, const float* ra, const void* b,
+                               int64_t ldb, const float* rb, int64_t M, int64_t N, int64_t K,
+                               void* out, int64_t ldo, int out_dtype, void* stream);
+
+/*
+ * FP8 blockwise linear layer, fwd / dgrad / wgrad ([INTEG] Summary:
+ * Float8BlockwiseLinear; [REPRO] review comments: 1x128 x 128x128 on the
+ * grad path, 1x128 x 1x128 for the weight gradient).  All tensors are
+ * contiguous row-major bf16: X[M, K], W[N, K], dY[M, N].
+ *   fwd:   Y[M, N]  = X . W^T   (X 1x128, W 128x128)        K % 128 == 0
+ *   dgrad: dX[M, K] = dY . W    (dY 1x128, W^T 128x128)     N % 128 == 0
+ *   wgrad: dW[N, K] = dY^T . X  (dY^T, X^T 1x128 along M)   M % 128 == 0
+ * Each quantizes its inputs into the caller's workspace (codes and
+ * reciprocal scales) and runs the blockwise GEMM; bf16 output.
+ * which = 0 fwd, 1 dgrad, 2 wgrad for the workspace query.  All dims must
+ * also be multiples of 16.
+ */
+size_t fp8bw_linear_ws_bytes(int64_t M, int64_t N, int64_t K, int which);
+int fp8_linear_fwd(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                   void* ws, size_t ws_bytes, void* stream);
+int fp8_linear_dgrad(const void* dy, const void* w, void* dx, int64_t M, int64_t N, int64_t K,
+                     void* ws, size_t ws_bytes, void* stream);
+int fp8_linear_wgrad(const void* dy, const void* x, void* dw, int64_t M, int64_t N, int64_t K,
+                     void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BW_H */

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fp8bw.h declares, and rejects invalid arguments on the host before
+any HIP call.  No compute call is made here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import blockwise_scaled_fp8_amd as fp8
+from blockwise_scaled_fp8_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bw.h")
+
+OK, NULL, SHAPE, LAYOUT, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5, 6
+P = 0x10000  # a 256-byte aligned fake device address; never dereferenced here
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z0-9_]+)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fp8.load_library()
+
+
+def test_library_exports_every_header_function(lib):
+    names = header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.PROTOTYPES), "binding prototypes must mirror the header"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.fp8bw_abi_version() == 1
+    for s, name in _lib.STATUS.items():
+        assert lib.fp8bw_status_str(s).decode() == name
+    assert lib.fp8bw_gemm_num_configs() >= 1
+
+
+def _quant(lib, **kw):
+    a = dict(x=P, rows=128, cols=256, ld_x=256, block=0, transpose=0, q=P, ld_q=256,
+             recip=P, rs_row=1, rs_kb=128, stream=None)
+    a.update(kw)
+    return lib.fp8_blockwise_quant(a["x"], a["rows"], a["cols"], a["ld_x"], a["block"],
+                                   a["transpose"], a["q"], a["ld_q"], a["recip"], a["rs_row"],
+                                   a["rs_kb"], a["stream"])
+
+
+def test_quant_validation(lib):
+    assert _quant(lib, block=2) == UNSUP
+    assert _quant(lib, transpose=2) == UNSUP
+    assert _quant(lib, rows=-1) == SHAPE
+    assert _quant(lib, cols=200) == SHAPE                 # not a multiple of 16
+    assert _quant(lib, transpose=1, rows=100) == SHAPE    # transposed rows % 16
+    assert _quant(lib, x=None) == NULL
+    assert _quant(lib, recip=None) == NULL
+    assert _quant(lib, x=P + 8) == ALIGN
+    assert _quant(lib, ld_x=200) == LAYOUT
+    assert _quant(lib, ld_x=260) == LAYOUT                # not a multiple of 8
+    assert _quant(lib, ld_q=264) == LAYOUT                # not a multiple of 16
+    assert _quant(lib, rs_row=1, rs_kb=64) == LAYOUT      # aliases rows
+    assert _quant(lib, rs_row=-1) == LAYOUT
+    assert "recip strides" in lib.fp8bw_last_error().decode()
+    # zero-sized problems are accepted and enqueue nothing (no HIP call)
+    assert _quant(lib, rows=0, x=None, q=None, recip=None) == OK
+    assert _quant(lib, cols=0, x=None, q=None, recip=None) == OK
+
+
+def _gemm(lib, fn="fp8_scaled_gemm_blockwise", **kw):
+    a = dict(a=P, lda=256, ra=P, ra_s_row=1, ra_s_kb=64, b=P, ldb=256, rb=P, rb_s_row=1,
+             rb_s_kb=1, b_block=1, M=64, N=128, K=256, out=P, ldo=128, out_dtype=0, ws=P,
+             ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    args = [a[k] for k in ("a", "lda", "ra", "ra_s_row", "ra_s_kb", "b", "ldb", "rb", "rb_s_row",
+                           "rb_s_kb", "b_block", "M", "N", "K", "out", "ldo", "out_dtype")]
+    if fn == "fp8_scaled_gemm_blockwise_cfg":
+        args += [a.get("config", -1), a.get("splits", 0)]
+    args += [a["ws"], a["ws_bytes"], a["stream"]]
+    return getattr(lib, fn)(*args)
+
+
+def test_gemm_validation(lib):
+    assert _gemm(lib, K=200) == SHAPE                    # K % 128
+    assert _gemm(lib, M=-1) == SHAPE
+    assert _gemm(lib, b_block=3) == UNSUP
+    assert _gemm(lib, out_dtype=5) == UNSUP
+    assert _gemm(lib, a=None) == NULL
+    assert _gemm(lib, rb=None) == NULL
+    assert _gemm(lib, b=P + 1) == ALIGN
+    assert _gemm(lib, lda=128) == LAYOUT                 # lda < K
+    assert _gemm(lib, ldb=264) == LAYOUT                 # not a multiple of 16
+    assert _gemm(lib, ldo=100) == LAYOUT                 # ldo < N
+    assert _gemm(lib, ra_s_row=2) == LAYOUT              # ra must be column-major
+    assert _gemm(lib, ra_s_kb=32) == LAYOUT              # aliases rows of ra
+    assert _gemm(lib, b_block=0, rb_s_row=2, rb_s_kb=256) == LAYOUT   # 1x128 rb column-major
+    assert _gemm(lib, rb_s_row=1, rb_s_kb=0) == LAYOUT   # 128x128 rb: aliases
+    assert _gemm(lib, M=0, a=None, b=None, out=None) == OK
+    assert _gemm(lib, "fp8_scaled_gemm_blockwise_cfg", config=99) == UNSUP
+    assert _gemm(lib, "fp8_scaled_gemm_blockwise_cfg", splits=-2) == SHAPE
+    assert _gemm(lib, "fp8_scaled_gemm_blockwise_cfg", splits=3) == SHAPE   # > 2 K blocks
+    need = lib.fp8bw_gemm_ws_bytes_for_split(64, 128, 2)
+    assert need == 2 * 64 * 128 * 4
+    assert _gemm(lib, "fp8_scaled_gemm_blockwise_cfg", splits=2, ws_bytes=need - 1) == WS
+    assert _gemm(lib, "fp8_scaled_gemm_blockwise_cfg", splits=2, ws=None) == WS
+
+
+def test_tensorwise_validation(lib):
+    f = lib.fp8_scaled_gemm_tensorwise
+    assert f(P, 32, P, P, 32, P, 16, 32, 24, P, 32, 1, None) == SHAPE        # K % 16
+    assert f(P, 32, None, P, 32, P, 16, 32, 32, P, 32, 1, None) == NULL
+    assert f(P, 32, P, P, 32, P, 16, 32, 32, P, 30, 1, None) == LAYOUT       # ldo < N
+    q = lib.fp8_tensorwise_quant
+    assert q(P, 16, 32, 32, P, 32, P, P, 0, None) == WS
+    assert q(P, 16, 30, 32, P, 32, P, P, 4096, None) == SHAPE
+    assert lib.fp8bw_tensorwise_quant_ws_bytes(16, 32) >= 4
+
+
+def test_linear_validation_and_workspace(lib):
+    for which, fn in enumerate(("fp8_linear_fwd", "fp8_linear_dgrad", "fp8_linear_wgrad")):
+        f = getattr(lib, fn)
+        need = lib.fp8bw_linear_ws_bytes(256, 256, 256, which)
+        assert need >= 2 * 256 * 256
+        assert f(P, P, P, 256, 256, 256, P, need - 1, None) == WS
+        assert f(P, P, P, 256, 256, 256, None, need, None) == WS
+        assert f(None, P, P, 256, 256, 256, P, need, None) == NULL
+        assert f(P, P, P, 256, 256, 200, P, need, None) == SHAPE
+        assert f(P, P, P, 256, 256, 256, P + 16, need, None) == ALIGN    # ws 256-aligned
+    # contraction axis must be a multiple of 128
+    assert lib.fp8_linear_fwd(P, P, P, 256, 256, 144, P, 1 << 24, None) == SHAPE
+    assert lib.fp8_linear_dgrad(P, P, P, 256, 144, 256, P, 1 << 24, None) == SHAPE
+    assert lib.fp8_linear_wgrad(P, P, P, 144, 256, 256, P, 1 << 24, None) == SHAPE
+
+
+def test_binding_raises_with_message(lib):
+    st = _gemm(lib, K=200)
+    with pytest.raises(fp8.FP8BWError, match="K % 128"):
+        _lib.check(st)
+
+
+def test_no_host_fallback_in_binding():
+    """The binding has no CPU path: ops refuse non-CUDA tensors."""
+    import torch
+    x = torch.zeros(16, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fp8.fp8_blockwise_quant(x)
+    assert ctypes.sizeof(ctypes.c_void_p) == 8

@@ -1,0 +1,226 @@
+"""GPU parity of the blockwise and tensorwise GEMMs against the oracle,
+called through the C ABI.  The GEMM inputs (codes and reciprocal scales) are
+produced by the oracle on the host and uploaded, so these tests isolate the
+GEMM; the linear tests run the whole GPU pipeline."""
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_scaled_fp8_amd as fp8
+from oracle import e4m3, gemm, metrics, quant
+from synth import inputs
+from tests.gpu_util import bits, check_gemm_output, host_f32, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _up_codes(c, dev):
+    return torch.from_numpy(np.ascontiguousarray(c)).to(dev)
+
+
+def _up_scales_colmajor(r, dev):
+    """Logical [ni, nj] float32 -> device tensor with column-major strides."""
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(r, np.float32).T)).to(dev)
+    return t.t()
+
+
+def _random_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E
+    return c
+
+
+def _run_blockwise(dev, aq, ar, bq, br, b_block, out_dtype, what, config=None, splits=None):
+    say("gemm blockwise", what, aq.shape, bq.shape, b_block, out_dtype, config, splits)
+    od = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = fp8.fp8_scaled_gemm_blockwise(_up_codes(aq, dev), _up_scales_colmajor(ar, dev),
+                                        _up_codes(bq, dev), _up_scales_colmajor(br, dev),
+                                        b_block=b_block, out_dtype=od, config=config,
+                                        splits=splits)
+    torch.cuda.synchronize()
+    ref, S = gemm.blockwise_gemm(aq, ar, bq, br, b_block, with_bound=True)
+    return check_gemm_output(host_f32(out), ref, S, aq.shape[1] // 128, out_dtype, what)
+
+
+def test_tiny_linear_shapes(gpu):
+    """X[128,512] N(0,1) x W[256,512] nn.Linear init, X 1x128 and W 128x128."""
+    x = bits(inputs.randn_bf16((128, 512), seed=inputs.tensor_seed(0, "x")))
+    w = bits(inputs.linear_weight_bf16(256, 512, seed=inputs.tensor_seed(0, "w")))
+    xq, xr = quant.quant_1x128(x)
+    wq, wr = quant.quant_128x128(w)
+    for od in ("bf16", "f32"):
+        _run_blockwise(gpu, xq, xr, wq, wr, "128x128", od, "tiny linear")
+
+
+@pytest.mark.parametrize("kb", [1, 2, 3, 5, 7])
+@pytest.mark.parametrize("mn", [(1, 16), (16, 96), (77, 130), (128, 256), (200, 300)])
+def test_blockwise_ragged_and_k_blocks(gpu, kb, mn):
+    rng = np.random.default_rng(kb * 1000 + mn[0])
+    M, N = mn
+    K = 128 * kb
+    aq = _random_codes(rng, (M, K))
+    bq = _random_codes(rng, (N, K))
+    ar = rng.uniform(0.5, 2.0, (M, kb)).astype(np.float32) * np.float32(2.0 ** -8)
+    for b_block in ("128x128", "1x128"):
+        nbr = N if b_block == "1x128" else -(-N // 128)
+        br = rng.uniform(0.5, 2.0, (nbr, kb)).astype(np.float32) * np.float32(2.0 ** -9)
+        _run_blockwise(gpu, aq, ar, bq, br, b_block, "bf16", f"M{M} N{N} kb{kb} {b_block}")
+        _run_blockwise(gpu, aq, ar, bq, br, b_block, "f32", f"M{M} N{N} kb{kb} {b_block}")
+
+
+def test_power_of_two_scale_probe(gpu):
+    """Distinct power-of-two scales per (row, kb) and per (block, kb): any
+    scale-indexing error shows up as an exact power-of-two discrepancy."""
+    rng = np.random.default_rng(3)
+    M, N, kb = 96, 272, 6
+    aq = _random_codes(rng, (M, 128 * kb))
+    bq = _random_codes(rng, (N, 128 * kb))
+    ar = np.array([[2.0 ** ((m % 13) - 6 + 2 * k) for k in range(kb)] for m in range(M)], np.float32)
+    for b_block in ("128x128", "1x128"):
+        nbr = N if b_block == "1x128" else 3
+        br = np.array([[2.0 ** (-(r % 11) - k) for k in range(kb)] for r in range(nbr)], np.float32)
+        _run_blockwise(gpu, aq, ar, bq, br, b_block, "f32", f"pow2 probe {b_block}")
+
+
+def test_every_config_and_split(gpu):
+    """Force every tile configuration and several split-K counts (a kernel
+    variant can be wrong where the others are right)."""
+    rng = np.random.default_rng(4)
+    M, N, kb = 200, 300, 8
+    aq = _random_codes(rng, (M, 128 * kb))
+    bq = _random_codes(rng, (N, 128 * kb))
+    ar = rng.uniform(0.01, 0.02, (M, kb)).astype(np.float32)
+    for b_block in ("128x128", "1x128"):
+        nbr = N if b_block == "1x128" else 3
+        br = rng.uniform(0.01, 0.02, (nbr, kb)).astype(np.float32)
+        for cfg in range(fp8.fp8bw_gemm_num_configs()):
+            for splits in (1, 2, 3, 8):
+                for od in ("bf16", "f32"):
+                    _run_blockwise(gpu, aq, ar, bq, br, b_block, od, f"cfg{cfg} split{splits}",
+                                   config=cfg, splits=splits)
+
+
+def test_canary_output_and_strided_b_scales(gpu):
+    """Output written with ldo > N into a canary-filled buffer; B scales given
+    row-major (strides (kb, 1)) instead of column-major."""
+    rng = np.random.default_rng(5)
+    M, N, kb = 130, 200, 3
+    aq = _random_codes(rng, (M, 128 * kb))
+    bq = _random_codes(rng, (N, 128 * kb))
+    ar = rng.uniform(0.01, 0.02, (M, kb)).astype(np.float32)
+    br = rng.uniform(0.01, 0.02, (2, kb)).astype(np.float32)
+    buf = torch.full((M, N + 24), float("nan"), dtype=torch.float32, device=gpu)
+    rb_rowmajor = torch.from_numpy(br).to(gpu)            # strides (kb, 1)
+    say("gemm canary")
+    fp8.fp8_scaled_gemm_blockwise(_up_codes(aq, gpu), _up_scales_colmajor(ar, gpu),
+                                  _up_codes(bq, gpu), rb_rowmajor, out=buf[:, :N])
+    torch.cuda.synchronize()
+    ref, S = gemm.blockwise_gemm(aq, ar, bq, br, "128x128", with_bound=True)
+    check_gemm_output(host_f32(buf[:, :N]), ref, S, kb, "f32", "canary")
+    assert np.all(np.isnan(host_f32(buf[:, N:])))
+
+
+def test_long_k_1000_1001_1002_blocks(gpu):
+    """M = N = 1024, K in {128000, 128128, 128256}: A N(0,1) 1x128, B nn.Linear
+    init 128x128, bf16 out, whole pipeline on the GPU.  Sampled outputs match
+    the oracle; SQNR vs the fp32 product stays in the band for all three
+    (the pages report a collapse of another library at 1001 / 1002)."""
+    M = N = 1024
+    results = {}
+    for K in (128000, 128128, 128256):
+        say("long-K", K, "generate")
+        a = inputs.randn_bf16((M, K), seed=inputs.tensor_seed(20, "a"), device="cuda")
+        b = inputs.linear_weight_bf16(N, K, seed=inputs.tensor_seed(20, "b"), device="cuda")
+        say("long-K", K, "gpu quant + gemm")
+        aq, ar = fp8.fp8_blockwise_quant(a, "1x128")
+        bq, br = fp8.fp8_blockwise_quant(b, "128x128")
+        out = fp8.fp8_scaled_gemm_blockwise(aq, ar, bq, br, "128x128")
+        torch.cuda.synchronize()
+        rows = np.sort(np.random.default_rng(K).choice(M, 24, replace=False))
+        nblk = (0, 5)
+        cols = np.concatenate([np.arange(n * 128, n * 128 + 128) for n in nblk])
+        say("long-K", K, "oracle on sample")
+        a_s = bits(a[torch.from_numpy(rows).to(a.device)])
+        oaq, oar = quant.quant_1x128(a_s)
+        b_s = bits(b[torch.from_numpy(cols).to(b.device)])
+        obq, obr = quant.quant_128x128(b_s)
+        ref, S = gemm.blockwise_gemm(oaq, oar, obq, obr, "128x128", with_bound=True)
+        got = host_f32(out)[np.ix_(rows, cols)]
+        check_gemm_output(got, ref, S, K // 128, "bf16", f"long-K {K}")
+        fp32ref = gemm.fp32_reference(a_s, b_s)
+        s_gpu = metrics.sqnr_db(fp32ref, got)
+        s_orc = metrics.sqnr_db(fp32ref, e4m3.rne_bf16(ref.astype(np.float32)))
+        assert 28.0 <= s_gpu <= 32.5, (K, s_gpu)
+        assert abs(s_gpu - s_orc) <= 0.05, (K, s_gpu, s_orc)
+        # no collapse anywhere in the full output: |out| ~ sqrt(M N / 3)
+        nrm = float(torch.linalg.vector_norm(out.float()))
+        assert 0.9 * np.sqrt(M * N / 3) < nrm < 1.1 * np.sqrt(M * N / 3), (K, nrm)
+        results[K] = s_gpu
+        del a, b, aq, bq, out
+    say("long-K SQNR dB", results)
+
+
+@pytest.mark.parametrize("splits", [1, 7, 13, 64])
+def test_long_k_forced_splits(gpu, splits):
+    """K = 128128 (1001 blocks, 7 x 11 x 13) with forced split counts that do
+    and do not divide the block count."""
+    rng = np.random.default_rng(splits)
+    M, N, K = 64, 256, 128128
+    aq = _random_codes(rng, (M, K))
+    bq = _random_codes(rng, (N, K))
+    ar = rng.uniform(1e-3, 2e-3, (M, K // 128)).astype(np.float32)
+    br = rng.uniform(1e-3, 2e-3, (2, K // 128)).astype(np.float32)
+    for cfg in range(fp8.fp8bw_gemm_num_configs()):
+        _run_blockwise(gpu, aq, ar, bq, br, "128x128", "f32", f"long-K splits={splits} cfg{cfg}",
+                       config=cfg, splits=splits)
+
+
+def _tensorwise_case(dev, M, N, K, out_dtype, seed):
+    x = bits(inputs.randn_bf16((M, K), seed=inputs.tensor_seed(seed, "x")))
+    w = bits(inputs.randn_bf16((N, K), seed=inputs.tensor_seed(seed, "w")))
+    xq, xr = quant.quant_tensorwise(x)
+    wq, wr = quant.quant_tensorwise(w)
+    od = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    say("gemm tensorwise", M, N, K, out_dtype)
+    out = fp8.fp8_scaled_gemm_tensorwise(_up_codes(xq, dev), torch.tensor([xr], device=dev),
+                                         _up_codes(wq, dev), torch.tensor([wr], device=dev),
+                                         out_dtype=od)
+    torch.cuda.synchronize()
+    ref = gemm.tensorwise_gemm(xq, xr, wq, wr)
+    S = gemm.tensorwise_bound(xq, xr, wq, wr)
+    got = host_f32(out)
+    check_gemm_output(got, ref, S, -(-K // 128), out_dtype, f"tensorwise {M}x{N}x{K}")
+    return got, ref
+
+
+def test_tensorwise_256x4096x1024(gpu):
+    got, ref = _tensorwise_case(gpu, 256, 4096, 1024, "bf16", seed=30)
+    # the checks the per-tensor issue applies, against the dequant reference
+    refb = torch.from_numpy(e4m3.rne_bf16(ref.astype(np.float32)))
+    g = torch.from_numpy(got)
+    for rtol, atol in ((1e-2, 1e-2), (5e-2, 5e-2)):
+        assert torch.allclose(g, refb, rtol=rtol, atol=atol)
+
+
+def test_tensorwise_edge_16x32x32_fp32(gpu):
+    got, ref = _tensorwise_case(gpu, 16, 32, 32, "f32", seed=31)
+    assert np.allclose(got, ref, rtol=0.01, atol=0.05)
+
+
+@pytest.mark.parametrize("mnk", [(1, 16, 16), (33, 17, 48), (130, 70, 400), (64, 64, 128)])
+def test_tensorwise_ragged(gpu, mnk):
+    _tensorwise_case(gpu, *mnk, "f32", seed=32 + mnk[0])
+
+
+def test_gemm_deterministic(gpu):
+    rng = np.random.default_rng(6)
+    aq = _up_codes(_random_codes(rng, (300, 1024)), gpu)
+    bq = _up_codes(_random_codes(rng, (260, 1024)), gpu)
+    ar = _up_scales_colmajor(rng.uniform(0.5, 1, (300, 8)).astype(np.float32), gpu)
+    br = _up_scales_colmajor(rng.uniform(0.5, 1, (3, 8)).astype(np.float32), gpu)
+    say("gemm determinism")
+    o1 = fp8.fp8_scaled_gemm_blockwise(aq, ar, bq, br, splits=4, config=0, out_dtype=torch.float32)
+    o2 = fp8.fp8_scaled_gemm_blockwise(aq, ar, bq, br, splits=4, config=0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))

@@ -1,0 +1,116 @@
+"""GPU parity of the FP8 linear wrapper (quantize + blockwise GEMM, all on the
+GPU, through the C ABI) against the oracle's composition."""
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_scaled_fp8_amd as fp8
+from oracle import e4m3, gemm, linear, metrics, quant
+from synth import inputs
+from tests.gpu_util import bits, check_gemm_output, host_f32, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(M, N, K, seed, device):
+    x = inputs.randn_bf16((M, K), seed=inputs.tensor_seed(seed, "x"), device=device)
+    w = inputs.linear_weight_bf16(N, K, seed=inputs.tensor_seed(seed, "w"), device=device)
+    dy = inputs.randn_bf16((M, N), seed=inputs.tensor_seed(seed, "dy"), device=device)
+    return x, w, dy
+
+
+@pytest.mark.parametrize("mnk", [(128, 256, 512), (256, 384, 640), (384, 128, 256), (128, 128, 128)])
+def test_linear_full_compare(gpu, mnk):
+    M, N, K = mnk
+    x, w, dy = _inputs(M, N, K, seed=1, device="cpu")
+    xb, wb, dyb = bits(x), bits(w), bits(dy)
+    xd, wd, dyd = x.to(gpu), w.to(gpu), dy.to(gpu)
+    say("linear fwd", mnk)
+    y = fp8.fp8_linear_fwd(xd, wd)
+    torch.cuda.synchronize()
+    ref, S = linear.fwd(xb, wb, with_bound=True)
+    check_gemm_output(host_f32(y), ref, S, K // 128, "bf16", f"fwd {mnk}")
+    say("linear dgrad", mnk)
+    dx = fp8.fp8_linear_dgrad(dyd, wd)
+    torch.cuda.synchronize()
+    ref, S = linear.dgrad(dyb, wb, with_bound=True)
+    check_gemm_output(host_f32(dx), ref, S, N // 128, "bf16", f"dgrad {mnk}")
+    say("linear wgrad", mnk)
+    dw = fp8.fp8_linear_wgrad(dyd, xd)
+    torch.cuda.synchronize()
+    ref, S = linear.wgrad(dyb, xb, with_bound=True)
+    check_gemm_output(host_f32(dw), ref, S, M // 128, "bf16", f"wgrad {mnk}")
+
+
+def _idx(t, rows=None, cols=None):
+    if rows is not None:
+        t = t[torch.from_numpy(rows).to(t.device)]
+    if cols is not None:
+        t = t[:, torch.from_numpy(cols).to(t.device)]
+    return bits(t)
+
+
+@pytest.mark.parametrize("mnk", [(16640, 5120, 8192), (16640, 8192, 5120)])
+def test_linear_llama4_shapes_sampled(gpu, mnk):
+    """Full-size fwd, dgrad and wgrad at the llama4 shapes; outputs checked
+    on sampled rows x two 128-column blocks, which the oracle computes from
+    the same bf16 inputs; SQNR of the sample vs the fp32 product in band."""
+    M, N, K = mnk
+    say("llama4 generate", mnk)
+    x, w, dy = _inputs(M, N, K, seed=2, device="cuda")
+    rng = np.random.default_rng(M + N)
+    rows = np.sort(rng.choice(M, 16, replace=False))
+    say("llama4 fwd", mnk)
+    y = fp8.fp8_linear_fwd(x, w)
+    torch.cuda.synchronize()
+    ncols = np.r_[np.arange(0, 128), np.arange(N - 128, N)]
+    xs, ws = _idx(x, rows=rows), _idx(w, rows=ncols)
+    ref, S = gemm.blockwise_gemm(*quant.quant_1x128(xs), *quant.quant_128x128(ws), "128x128",
+                                 with_bound=True)
+    got = host_f32(y)[np.ix_(rows, ncols)]
+    check_gemm_output(got, ref, S, K // 128, "bf16", f"fwd {mnk}")
+    assert 27.5 < metrics.sqnr_db(gemm.fp32_reference(xs, ws), got) < 32.5
+    del y
+    say("llama4 dgrad", mnk)
+    dx = fp8.fp8_linear_dgrad(dy, w)
+    torch.cuda.synchronize()
+    kcols = np.r_[np.arange(128, 256), np.arange(K - 128, K)]
+    dys = _idx(dy, rows=rows)
+    wcols = _idx(w, cols=kcols)                    # W[:, kcols] -> [N, 256]
+    ref, S = gemm.blockwise_gemm(*quant.quant_1x128(dys), *quant.quant_128x128_transposed(wcols),
+                                 "128x128", with_bound=True)
+    got = host_f32(dx)[np.ix_(rows, kcols)]
+    check_gemm_output(got, ref, S, N // 128, "bf16", f"dgrad {mnk}")
+    del dx
+    say("llama4 wgrad", mnk)
+    dw = fp8.fp8_linear_wgrad(dy, x)
+    torch.cuda.synchronize()
+    nrows = np.sort(rng.choice(N, 16, replace=False))
+    dycols = _idx(dy, cols=nrows)                  # dY[:, n] -> [M, 16]
+    xcols = _idx(x, cols=kcols)                    # X[:, k]  -> [M, 256]
+    ref, S = gemm.blockwise_gemm(*quant.quant_1x128_along_rows(dycols),
+                                 *quant.quant_1x128_along_rows(xcols), "1x128", with_bound=True)
+    got = host_f32(dw)[np.ix_(nrows, kcols)]
+    check_gemm_output(got, ref, S, M // 128, "bf16", f"wgrad {mnk}")
+    fp32 = (e4m3.bf16_bits_to_f32(dycols).astype(np.float64).T
+            @ e4m3.bf16_bits_to_f32(xcols).astype(np.float64))
+    assert 27.5 < metrics.sqnr_db(fp32, got) < 32.5
+
+
+def test_linear_shared_workspace_reuse(gpu):
+    """One workspace reused across fwd, dgrad and wgrad calls in a row."""
+    M, N, K = 256, 256, 384
+    x, w, dy = _inputs(M, N, K, seed=3, device="cpu")
+    need = max(fp8.load_library().fp8bw_linear_ws_bytes(M, N, K, i) for i in range(3))
+    ws = torch.empty(need, dtype=torch.uint8, device=gpu)
+    say("linear workspace reuse")
+    y = fp8.fp8_linear_fwd(x.to(gpu), w.to(gpu), ws=ws)
+    dx = fp8.fp8_linear_dgrad(dy.to(gpu), w.to(gpu), ws=ws)
+    dw = fp8.fp8_linear_wgrad(dy.to(gpu), x.to(gpu), ws=ws)
+    torch.cuda.synchronize()
+    for got, (ref, S), kb, name in (
+            (y, linear.fwd(bits(x), bits(w), True), K // 128, "fwd"),
+            (dx, linear.dgrad(bits(dy), bits(w), True), N // 128, "dgrad"),
+            (dw, linear.wgrad(bits(dy), bits(x), True), M // 128, "wgrad")):
+        check_gemm_output(host_f32(got), ref, S, kb, "bf16", name)
