@@ -19,8 +19,8 @@ MIN_NORMAL = 2.0 ** -6
 MIN_SUBNORMAL = 2.0 ** -9
 
 
-def decode(codes):
-    """E4M3 codes (uint8) -> exact float64 values; NaN codes -> nan.  [OCP]"""
+def _decode_formula(codes):
+    """E4M3 codes -> exact float64 values by the OCP definition; NaN codes -> nan."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     neg = (c & 0x80) != 0
     e = (c >> 3) & 0xF
@@ -30,6 +30,16 @@ def decode(codes):
                    np.ldexp(1.0 + m / 8.0, (e - EXP_BIAS).astype(np.int64)))
     val = np.where(neg, -mag, mag)
     return np.where((e == 15) & ((c & 0x7) == 7), np.nan, val)
+
+
+# All 256 code values, from the definition above.
+DECODE_TABLE = _decode_formula(np.arange(256))
+
+
+def decode(codes):
+    """E4M3 codes (uint8) -> exact float64 values; NaN codes -> nan.  [OCP]
+    (A lookup into DECODE_TABLE, the definition evaluated for every code.)"""
+    return DECODE_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def encode_rne(v):
