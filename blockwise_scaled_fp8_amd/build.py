@@ -24,6 +24,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["quant.hip", "gemm.hip", "api.cpp"]
+# Per-source extra flags.  gemm.hip: select the VGPR form of MFMA so the
+# rescale's VALU reads the MFMA results without AGPR->VGPR copies.
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 FLAGS = [
     f"--offload-arch={ARCH}",
@@ -57,7 +60,8 @@ def build(verbose=False, jobs=None):
         obj = os.path.join(BUILD_DIR, src + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs or min(8, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():

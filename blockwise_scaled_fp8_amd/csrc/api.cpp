@@ -212,7 +212,8 @@ static int gemm_blockwise_impl(const void* a, int64_t lda, const float* ra, int6
   int cfg = 0, sp = 1;
   fp8bw::gemm_choose(p, &cfg, &sp);
   if (config >= 0) {
-    if (!fp8bw::gemm_config_ok(p, config)) return fail(FP8BW_ERR_UNSUPPORTED, "config %d not available", config);
+    if (!fp8bw::gemm_config_ok(p, config))
+      return fail(FP8BW_ERR_UNSUPPORTED, "config %d does not support this problem", config);
     cfg = config;
   }
   if (splits > 0) sp = splits;

@@ -231,6 +231,275 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel: BM x BN workgroup tile, WGM x WGN waves, STAGES-deep
+// LDS ring filled by direct global->LDS loads (global_load_lds_dwordx4: each
+// lane's 16 bytes land at LDS base + 16 * lane, so a wave instruction fills
+// one 1 KB "row octet" = 8 rows x 128 bytes; the XOR swizzle is applied by
+// choosing which global chunk each lane fetches).  Scales ride the same ring
+// via 4-byte direct loads.  The compiler does not order these LDS writes
+// against later LDS reads, so the kernel waits with explicit vmcnt counts:
+// every wave issues exactly LPS loads per stage, and before consuming stage
+// kb+1 it waits until at most the loads of later stages are outstanding.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with vmcnt = N and no wait on expcnt / lgkmcnt (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Tile order: XCD-aware (the dispatcher deals workgroups round-robin to the
+// 8 XCDs; give each XCD a contiguous range of tile ids) then grouped
+// (GROUP_M row-blocks per column sweep) so that concurrently running tiles
+// on one XCD share A and B slices in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n,
+                                            int* tm, int* tn) {
+  constexpr int kXcds = 8, kGroupM = 8;
+  const int x = bid % kXcds, q = bid / kXcds;
+  const int full = nwg / kXcds, rem = nwg % kXcds;
+  const int tile = x * full + min(x, rem) + q;
+  const int per_group = kGroupM * tiles_n;
+  const int group = tile / per_group;
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = tile - group * per_group;
+  *tm = first_m + in_group % gm;
+  *tn = in_group / gm;
+}
+
+// One stage of direct global->LDS loads for K block kb (see gemm_v2_kernel).
+template <int AI, int BI, int RAI, int RBI, int RAB, int RBB, int NW, int MODE>
+__device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* sa, uint8_t* sb,
+                                            float* sra, float* srb, const uint32_t (&aoff)[AI],
+                                            const uint32_t (&boff)[BI], int wave, int lane,
+                                            int m0, int n0) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel stub
+  const uint8_t* ga = p.a + (int64_t)kb * 128;
+  const uint8_t* gb = p.b + (int64_t)kb * 128;
+#pragma unroll
+  for (int i = 0; i < AI; ++i)
+    __builtin_amdgcn_global_load_lds(ga + aoff[i], (lds_void_t*)(sa + (wave + NW * i) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < BI; ++i)
+    __builtin_amdgcn_global_load_lds(gb + boff[i], (lds_void_t*)(sb + (wave + NW * i) * 1024), 16, 0, 0);
+  if constexpr (MODE != kTensorwise) {
+#pragma unroll
+    for (int i = 0; i < RAI; ++i) {
+      const int blk = (wave + NW * i) % RAB;
+      const int r = min(m0 + 64 * blk + lane, p.M - 1);
+      __builtin_amdgcn_global_load_lds(p.ra + (int64_t)kb * p.ra_s_kb + r,
+                                       (lds_void_t*)(sra + 64 * blk), 4, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < RBI; ++i) {
+      if constexpr (MODE == kBlockB128) {
+        const int nb = min(n0 / 128 + lane, (p.N - 1) / 128);
+        __builtin_amdgcn_global_load_lds(p.rb + (int64_t)nb * p.rb_s_row + (int64_t)kb * p.rb_s_kb,
+                                         (lds_void_t*)srb, 4, 0, 0);
+      } else {
+        const int blk = (wave + NW * i) % RBB;
+        const int c = min(n0 + 64 * blk + lane, p.N - 1);
+        __builtin_amdgcn_global_load_lds(p.rb + (int64_t)kb * p.rb_s_kb + c,
+                                         (lds_void_t*)(srb + 64 * blk), 4, 0, 0);
+      }
+    }
+  }
+#endif
+}
+
+template <bool GUARD, int TM, int TN, int MODE, int OUT, bool SPLIT>
+__device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM][TN], float tscale,
+                                          int mb, int nb, int frow, int fhalf) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = nb + 16 * j + frow;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mb + 16 * i + 4 * fhalf + v;
+        if (!GUARD || (m < p.M && n < p.N)) {
+          float val = acc[i][j][v];
+          if constexpr (MODE == kTensorwise) val *= tscale;
+          if constexpr (SPLIT) {
+            p.partial[((int64_t)blockIdx.y * p.M + m) * p.N + n] = val;
+          } else if constexpr (OUT == kOutBf16) {
+            ((uint16_t*)p.out)[(int64_t)m * p.ldo + n] = (uint16_t)f32_to_bf16_rne(val);
+          } else {
+            ((float*)p.out)[(int64_t)m * p.ldo + n] = val;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, int MODE, int OUT, bool SPLIT>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs p) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int AOCT = BM / 8, BOCT = BN / 8;
+  static_assert(AOCT % NW == 0 && BOCT % NW == 0, "row octets must split evenly over waves");
+  constexpr int AI = AOCT / NW, BI = BOCT / NW;
+  constexpr bool SCALED = MODE != kTensorwise;
+  constexpr int RAB = BM / 64;                       // 64-row blocks of ra
+  constexpr int RAI = SCALED ? (RAB + NW - 1) / NW : 0;
+  constexpr int RBB = MODE == kBlockB1x128 ? BN / 64 : 1;
+  constexpr int RBI = SCALED ? (RBB + NW - 1) / NW : 0;
+  constexpr int LPS = AI + BI + RAI + RBI;           // loads per wave per stage
+  constexpr int SBS = MODE == kBlockB1x128 ? BN : 64;
+  static_assert(STAGES == 2 || STAGES == 3, "2 or 3 stages");
+  static_assert(TN >= 2, "the rescale ring assumes at least two column sub-tiles");
+  static_assert(LPS < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[STAGES][BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[STAGES][BN * 128];
+  __shared__ __attribute__((aligned(16))) float sRa[SCALED ? STAGES : 1][SCALED ? BM : 4];
+  __shared__ __attribute__((aligned(16))) float sRb[SCALED ? STAGES : 1][SCALED ? SBS : 4];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kb_begin = blockIdx.y * p.kb_per_split;
+  const int kb_end = min(p.kblocks, kb_begin + p.kb_per_split);
+
+  // Per-lane global byte offsets of this wave's row octets (k offset added
+  // per stage).  Row r of an octet sits in lane 8 (r & 7) + c; lane's
+  // physical chunk c holds logical chunk c ^ (r & 7).
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;
+  uint32_t aoff[AI], boff[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int r = min(m0 + 8 * (wave + NW * i) + lrow, p.M - 1);
+    aoff[i] = (uint32_t)((int64_t)r * p.lda) + lchunk * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int r = min(n0 + 8 * (wave + NW * i) + lrow, p.N - 1);
+    boff[i] = (uint32_t)((int64_t)r * p.ldb) + lchunk * 16;
+  }
+
+#define FP8BW_ISSUE(kb, st)                                                                  \
+  issue_stage<AI, BI, RAI, RBI, RAB, RBB, NW, MODE>(p, (kb), sA[st], sB[st], sRa[SCALED ? (st) : 0], \
+                                                    sRb[SCALED ? (st) : 0], aoff, boff, wave,  \
+                                                    lane, m0, n0)
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int frow = lane & 15, fhalf = lane >> 4;
+  const int nkb = kb_end - kb_begin;
+  // Every iteration issues one stage of loads, STAGES-1 K blocks ahead; past
+  // the end it re-loads the last K block into a stage nobody reads again, so
+  // the loop body has no branches (one scheduling region) and every wave
+  // always has exactly LPS loads per stage in flight.
+  const int kb_last = kb_end - 1;
+
+  if (nkb > 0) {
+    FP8BW_ISSUE(kb_begin, 0);
+    if constexpr (STAGES == 3) {
+      FP8BW_ISSUE(min(kb_begin + 1, kb_last), 1);
+      wait_vmcnt<LPS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+  }
+  for (int it = 0; it < nkb; ++it) {
+    const int st = it % STAGES;
+    FP8BW_ISSUE(min(kb_begin + it + STAGES - 1, kb_last), (it + STAGES - 1) % STAGES);
+
+    v8i bf[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[j] = load_frag(sB[st], wn0 + 16 * j + frow, fhalf);
+    float sbn = 0.f;
+    float sbc[TN];
+    if constexpr (MODE == kBlockB128) sbn = sRb[st][(n0 + wn0) / 128 - n0 / 128];
+    if constexpr (MODE == kBlockB1x128) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sbc[j] = sRb[st][wn0 + 16 * j + frow];
+    }
+    // MFMA-granularity pipeline over the TM x TN sub-tiles (row-major): the
+    // partial of sub-tile t lands in ring slot t % 3 and is folded into its
+    // accumulator two MFMAs later, when it is complete, so each MFMA issues
+    // with the previous partials' rescale FMAs in its shadow.
+    constexpr int T = TM * TN;
+    v8i af[2];
+    v4f sa[2];
+    af[0] = load_frag(sA[st], wm0 + frow, fhalf);
+    if constexpr (SCALED) {
+      sa[0] = *(const v4f*)&sRa[st][wm0 + 4 * fhalf];
+      if constexpr (MODE == kBlockB128) sa[0] = sa[0] * sbn;
+    }
+    v4f ring[3];
+#pragma unroll
+    for (int t = 0; t < T + 2; ++t) {
+      const int i = t / TN, j = t % TN;
+      if (t < T) {
+        if (MODE == kTensorwise)
+          acc[i][j] = mfma_fp8(af[i & 1], bf[j], acc[i][j]);
+        else
+          ring[t % 3] = mfma_fp8(af[i & 1], bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+      }
+      if constexpr (SCALED) {
+        if (t >= 2) {
+          const int u = t - 2, iu = u / TN, ju = u % TN;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if constexpr (MODE == kBlockB128)
+              acc[iu][ju][v] = __builtin_fmaf(ring[u % 3][v], sa[iu & 1][v], acc[iu][ju][v]);
+            else
+              acc[iu][ju][v] = __builtin_fmaf(ring[u % 3][v] * sbc[ju], sa[iu & 1][v], acc[iu][ju][v]);
+          }
+        }
+      }
+      // Prefetch row i+1 into the slot of row i-1 only after the last
+      // rescale of row i-1 (step i*TN + 1) has read its scales.
+      if (t < T && j == 1 && i + 1 < TM) {
+        af[(i + 1) & 1] = load_frag(sA[st], wm0 + 16 * (i + 1) + frow, fhalf);
+        if constexpr (SCALED) {
+          sa[(i + 1) & 1] = *(const v4f*)&sRa[st][wm0 + 16 * (i + 1) + 4 * fhalf];
+          if constexpr (MODE == kBlockB128) sa[(i + 1) & 1] = sa[(i + 1) & 1] * sbn;
+        }
+      }
+      if constexpr (SCALED) {
+        if (t < T) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, MODE == kBlockB1x128 ? 8 : 4, 0);
+        }
+      }
+    }
+    if constexpr (STAGES == 3)
+      wait_vmcnt<LPS>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  }
+  wait_vmcnt<0>();
+
+  float tscale = 1.f;
+  if constexpr (MODE == kTensorwise) tscale = p.ra[0] * p.rb[0];
+  // Interior tiles store without per-element checks; edge tiles check rows
+  // and columns.
+  if (m0 + BM <= p.M && n0 + BN <= p.N)
+    store_acc<false, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, m0 + wm0, n0 + wn0, frow, fhalf);
+  else
+    store_acc<true, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, m0 + wm0, n0 + wn0, frow, fhalf);
+}
+#undef FP8BW_ISSUE
+
 // Sum the split partials in split order and convert.
 template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
@@ -268,16 +537,30 @@ hipError_t launch_zero_bf16(void* out, int64_t rows, int64_t cols, hipStream_t s
 // Config table.
 struct Cfg {
   int bm, bn;
+  int kind;   // 0: small-tile kernel, 1: large-tile kernel
 };
 static const Cfg kCfgs[] = {
-    {128, 128},
-    {64, 64},
+    {128, 128, 0},   // 0: 4 waves of 64x64, register-staged double buffer
+    {64, 64, 0},     // 1: small problems and tails
+    {256, 128, 1},   // 2: 4 waves of 128x64, 3-stage direct-to-LDS ring
+    {256, 256, 1},   // 3: 8 waves (2 per SIMD) of 128x64, 2-stage ring
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 int gemm_num_configs() { return kNumCfgs; }
 
-bool gemm_config_ok(const GemmProblem&, int cfg) { return cfg >= 0 && cfg < kNumCfgs; }
+bool gemm_config_ok(const GemmProblem& p, int cfg) {
+  if (cfg < 0 || cfg >= kNumCfgs) return false;
+  if (kCfgs[cfg].kind == 1) {
+    // The large-tile kernels load whole 128-byte K blocks (no K tail) and
+    // address operands with 32-bit byte offsets.
+    if (p.K % 128) return false;
+    if ((p.M - 1) * p.lda + p.K >= ((int64_t)1 << 32) ||
+        (p.N - 1) * p.ldb + p.K >= ((int64_t)1 << 32))
+      return false;
+  }
+  return true;
+}
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int splits) {
   return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
@@ -285,8 +568,16 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int splits) {
 
 void gemm_choose(const GemmProblem& p, int* config, int* splits) {
   const int64_t kblocks = (p.K + 127) / 128;
-  const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128);
-  int cfg = (t128 >= 128 || (p.M >= 128 && p.N >= 128 && t128 >= 64)) ? 0 : 1;
+  int cfg;
+  const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (p.M >= 256 && p.N >= 256 && t256 >= 128 && gemm_config_ok(p, 3))
+    cfg = 3;
+  else if (p.M >= 256 && p.N >= 128 && gemm_config_ok(p, 2))
+    cfg = 2;
+  else if (p.M >= 128 && p.N >= 128)
+    cfg = 0;
+  else
+    cfg = 1;
   const int bm = kCfgs[cfg].bm, bn = kCfgs[cfg].bn;
   const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
   int s = 1;
@@ -300,6 +591,29 @@ void gemm_choose(const GemmProblem& p, int* config, int* splits) {
   }
   *config = cfg;
   *splits = s;
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, int MODE>
+static hipError_t launch_v2(const GemmArgs& a, int splits, int out_kind, hipStream_t stream) {
+  dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits);
+  dim3 block(64 * WGM * WGN);
+  if (splits > 1)
+    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutF32, true>), grid, block, 0, stream, a);
+  else if (out_kind == kOutBf16)
+    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutBf16, false>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutF32, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int STAGES>
+static hipError_t launch_v2_mode(const GemmArgs& a, int mode, int splits, int out_kind,
+                                 hipStream_t stream) {
+  switch (mode) {
+    case kBlockB128: return launch_v2<BM, BN, WGM, WGN, STAGES, kBlockB128>(a, splits, out_kind, stream);
+    case kBlockB1x128: return launch_v2<BM, BN, WGM, WGN, STAGES, kBlockB1x128>(a, splits, out_kind, stream);
+    default: return launch_v2<BM, BN, WGM, WGN, STAGES, kTensorwise>(a, splits, out_kind, stream);
+  }
 }
 
 template <int BM, int BN, int MODE>
@@ -352,7 +666,9 @@ hipError_t launch_gemm(const GemmProblem& p, int cfg, int splits, void* ws, hipS
   hipError_t e;
   switch (cfg) {
     case 0: e = launch_mode<128, 128>(a, p.mode, splits, p.out_kind, stream); break;
-    default: e = launch_mode<64, 64>(a, p.mode, splits, p.out_kind, stream); break;
+    case 1: e = launch_mode<64, 64>(a, p.mode, splits, p.out_kind, stream); break;
+    case 2: e = launch_v2_mode<256, 128, 2, 2, 3>(a, p.mode, splits, p.out_kind, stream); break;
+    default: e = launch_v2_mode<256, 256, 2, 4, 2>(a, p.mode, splits, p.out_kind, stream); break;
   }
   if (e != hipSuccess || splits <= 1) return e;
   const int64_t total = p.M * p.N;
