@@ -16,10 +16,10 @@
 //    16x16 output sub-tile.  Its fp32 result P goes to a fresh accumulator
 //    and is folded into the running sum with one FMA per element:
 //    acc += P * (ra * rb).  The tensorwise variant accumulates in the MFMA.
-//  * A and B tiles for one K block are staged in LDS, double buffered, with
-//    the 16-byte chunk index XOR-swizzled by (row & 7) so both the 16-byte
-//    global->LDS writes and the 16-byte fragment reads are bank-conflict
-//    free.  The scales of the K block travel with the tile through LDS.
+//  * A and B tiles for one K block are staged in LDS with the 16-byte chunk
+//    index XOR-swizzled by row (see swz) so both the 16-byte global->LDS
+//    writes and the 16-byte fragment reads are bank-conflict free.  The
+//    scales of the K block travel with the tile through LDS.
 //  * Each lane feeds the MFMA 32 contiguous K bytes of its row for both A
 //    and B (the same byte->k assignment on both sides, so the dot product
 //    is over matching k whatever order the instruction uses internally).
@@ -55,10 +55,19 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// LDS tile layout: rows of 128 K-bytes; the logical 16-byte chunk c of row r
+// is stored at physical chunk c ^ swz(r).  gfx950's LDS serves 16 lanes per
+// cycle from 64 four-byte banks, and a fragment read has 16 consecutive
+// lanes on 16 consecutive rows at one logical chunk: rows 128 bytes apart
+// alternate between the two 32-bank halves, so swz must differ among the 8
+// even rows and among the 8 odd rows -- (r >> 1) & 7 does.  (r & 7 would put
+// rows r and r+8 on the same banks.)
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
 __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int half) {
-  // 32 K-bytes of `row`: 16-byte chunks 2*half and 2*half+1, swizzled.
-  const int c0 = (2 * half) ^ (row & 7);
-  const int c1 = (2 * half + 1) ^ (row & 7);
+  // 32 K-bytes of `row`: logical 16-byte chunks 2*half and 2*half+1.
+  const int c0 = (2 * half) ^ swz(row);
+  const int c1 = (2 * half + 1) ^ swz(row);
   const uint4 lo = *(const uint4*)(tile + row * 128 + (c0 << 4));
   const uint4 hi = *(const uint4*)(tile + row * 128 + (c1 << 4));
   v8i f;
@@ -136,12 +145,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int r = lrow + 32 * i;
-      *(uint4*)(&sA[buf][r * 128 + ((lc ^ (r & 7)) << 4)]) = rA[i];
+      *(uint4*)(&sA[buf][r * 128 + ((lc ^ swz(r)) << 4)]) = rA[i];
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
       const int r = lrow + 32 * i;
-      *(uint4*)(&sB[buf][r * 128 + ((lc ^ (r & 7)) << 4)]) = rB[i];
+      *(uint4*)(&sB[buf][r * 128 + ((lc ^ swz(r)) << 4)]) = rB[i];
     }
     if (MODE != kTensorwise) {
       if (tid < BM) sRa[buf][tid] = rsa;
@@ -372,10 +381,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const int kb_end = min(p.kblocks, kb_begin + p.kb_per_split);
 
   // Per-lane global byte offsets of this wave's row octets (k offset added
-  // per stage).  Row r of an octet sits in lane 8 (r & 7) + c; lane's
-  // physical chunk c holds logical chunk c ^ (r & 7).
+  // per stage).  Lane 8q + c of a DMA instruction fills physical chunk c of
+  // row 8o + q (o = octet index), which holds logical chunk c ^ swz(8o + q);
+  // swz(8o + q) = (4 (o & 1) + (q >> 1)) & 7 and o & 1 == wave & 1 because
+  // the octets of a wave step by NW (even).
+  static_assert(NW % 2 == 0, "octet parity must be the wave parity");
   const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
+  const int lchunk = (lane & 7) ^ ((4 * (wave & 1) + (lrow >> 1)) & 7);
   uint32_t aoff[AI], boff[BI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
