@@ -209,44 +209,45 @@ static int gemm_blockwise_impl(const void* a, int64_t lda, const float* ra, int6
   p.out = out; p.ldo = ldo; p.M = M; p.N = N; p.K = K;
   p.mode = b_block == FP8BW_BLOCK_128x128 ? fp8bw::kBlockB128 : fp8bw::kBlockB1x128;
   p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
-  int cfg = 0, sp = 1;
-  fp8bw::gemm_choose(p, &cfg, &sp);
-  if (config >= 0) {
-    if (!fp8bw::gemm_config_ok(p, config))
-      return fail(FP8BW_ERR_UNSUPPORTED, "config %d does not support this problem", config);
-    cfg = config;
+  if (config >= 0 && !fp8bw::gemm_config_ok(p, config))
+    return fail(FP8BW_ERR_UNSUPPORTED, "config %d does not support this problem", config);
+  if (splits > kMaxGridY || (kb > 0 && splits > kb) || (kb == 0 && splits > 1))
+    return fail(FP8BW_ERR_SHAPE, "splits=%d must be <= the number of K blocks (%lld)", splits, (long long)kb);
+  fp8bw::GemmPlan plan = fp8bw::gemm_plan(p, config, splits, true);
+  if (splits == 0 && plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) {
+    // The built-in plan wanted scratch the caller did not provide: run
+    // without splitting (same result up to rounding order, no workspace).
+    plan = fp8bw::gemm_plan(p, config, 0, false);
   }
-  if (splits > 0) sp = splits;
-  if (sp > kMaxGridY || (kb > 0 && sp > kb) || (kb == 0 && sp > 1))
-    return fail(FP8BW_ERR_SHAPE, "splits=%d must be <= the number of K blocks (%lld)", sp, (long long)kb);
-  const size_t need = fp8bw::gemm_ws_bytes(M, N, sp);
-  if (need > 0) {
-    if (!ws || ws_bytes < need) return fail(FP8BW_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (plan.ws_bytes > 0) {
+    if (!ws || ws_bytes < plan.ws_bytes)
+      return fail(FP8BW_ERR_WORKSPACE, "workspace needs %zu bytes", plan.ws_bytes);
     if (!aligned(ws, 16)) return fail(FP8BW_ERR_ALIGN, "ws must be 16-byte aligned");
   }
-  return hip_status(fp8bw::launch_gemm(p, cfg, sp, ws, (hipStream_t)stream), "fp8_scaled_gemm_blockwise");
-}
-
-static fp8bw::GemmProblem size_only_problem(int64_t M, int64_t N, int64_t K) {
-  fp8bw::GemmProblem p = {};
-  p.M = M; p.N = N; p.K = K;
-  p.mode = fp8bw::kBlockB128;
-  return p;
+  return hip_status(fp8bw::launch_gemm(p, plan, ws, (hipStream_t)stream), "fp8_scaled_gemm_blockwise");
 }
 
 FP8BW_API size_t fp8bw_gemm_blockwise_ws_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  fp8bw::GemmProblem p = size_only_problem(M, N, K);
-  int cfg = 0, sp = 1;
-  fp8bw::gemm_choose(p, &cfg, &sp);
-  return fp8bw::gemm_ws_bytes(M, N, sp);
+  // Upper bound over every configuration's built-in plan (the configuration
+  // chosen for a call also depends on its leading dimensions).
+  fp8bw::GemmProblem p = {};
+  p.M = M; p.N = N; p.K = K; p.lda = K; p.ldb = K;
+  p.mode = fp8bw::kBlockB128;
+  size_t need = 0;
+  for (int c = 0; c < fp8bw::gemm_num_configs(); ++c) {
+    if (!fp8bw::gemm_config_ok(p, c)) continue;
+    const size_t b = fp8bw::gemm_plan(p, c, 0, true).ws_bytes;
+    if (b > need) need = b;
+  }
+  return need;
 }
 
 FP8BW_API int fp8bw_gemm_num_configs(void) { return fp8bw::gemm_num_configs(); }
 
 FP8BW_API size_t fp8bw_gemm_ws_bytes_for_split(int64_t M, int64_t N, int splits) {
-  if (M <= 0 || N <= 0) return 0;
-  return fp8bw::gemm_ws_bytes(M, N, splits);
+  if (M <= 0 || N <= 0 || splits <= 1) return 0;
+  return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
 FP8BW_API int fp8_scaled_gemm_blockwise(const void* a, int64_t lda, const float* ra,
@@ -289,9 +290,9 @@ FP8BW_API int fp8_scaled_gemm_tensorwise(const void* a, int64_t lda, const float
   p.out = out; p.ldo = ldo; p.M = M; p.N = N; p.K = K;
   p.mode = fp8bw::kTensorwise;
   p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
-  int cfg = 0, sp = 1;
-  fp8bw::gemm_choose(p, &cfg, &sp);
-  return hip_status(fp8bw::launch_gemm(p, cfg, 1, nullptr, (hipStream_t)stream), "fp8_scaled_gemm_tensorwise");
+  // No workspace argument: never split.
+  const fp8bw::GemmPlan plan = fp8bw::gemm_plan(p, -1, 0, false);
+  return hip_status(fp8bw::launch_gemm(p, plan, nullptr, (hipStream_t)stream), "fp8_scaled_gemm_tensorwise");
 }
 
 // ---------------------------------------------------------------------------

@@ -47,6 +47,12 @@ struct GemmArgs {
   int kblocks;
   int tiles_m, tiles_n;
   int kb_per_split;
+  // Large-tile kernel only: this launch covers grouped tile ids
+  // [tile_base, tile_base + gridDim.x); with part_tiled the split partials
+  // are stored tile-locally, [split][tile - tile_base][BM][BN], instead of
+  // [split][M][N].
+  int tile_base;
+  int part_tiled;
 };
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
@@ -262,15 +268,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Tile order: XCD-aware (the dispatcher deals workgroups round-robin to the
-// 8 XCDs; give each XCD a contiguous range of tile ids) then grouped
-// (GROUP_M row-blocks per column sweep) so that concurrently running tiles
-// on one XCD share A and B slices in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n,
-                                            int* tm, int* tn) {
-  constexpr int kXcds = 8, kGroupM = 8;
-  const int x = bid % kXcds, q = bid / kXcds;
-  const int full = nwg / kXcds, rem = nwg % kXcds;
-  const int tile = x * full + min(x, rem) + q;
+// 8 XCDs; xcd_remap gives each XCD a contiguous range of tile ids) then
+// grouped (tile_to_mn: GROUP_M row-blocks per column sweep) so that
+// concurrently running tiles on one XCD share A and B slices in that XCD's
+// L2.
+__device__ __forceinline__ void tile_to_mn(int tile, int tiles_m, int tiles_n, int* tm, int* tn) {
+  constexpr int kGroupM = 8;
   const int per_group = kGroupM * tiles_n;
   const int group = tile / per_group;
   const int first_m = group * kGroupM;
@@ -278,6 +281,13 @@ __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int t
   const int in_group = tile - group * per_group;
   *tm = first_m + in_group % gm;
   *tn = in_group / gm;
+}
+
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+  constexpr int kXcds = 8;
+  const int x = bid % kXcds, q = bid / kXcds;
+  const int full = nwg / kXcds, rem = nwg % kXcds;
+  return x * full + min(x, rem) + q;
 }
 
 // One stage of direct global->LDS loads for K block kb (see gemm_v2_kernel).
@@ -322,7 +332,8 @@ __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* 
 
 template <bool GUARD, int TM, int TN, int MODE, int OUT, bool SPLIT>
 __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM][TN], float tscale,
-                                          int mb, int nb, int frow, int fhalf) {
+                                          int mb, int nb, int frow, int fhalf, float* pbase,
+                                          int64_t pld, int pm0, int pn0) {
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -335,7 +346,7 @@ __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM
           float val = acc[i][j][v];
           if constexpr (MODE == kTensorwise) val *= tscale;
           if constexpr (SPLIT) {
-            p.partial[((int64_t)blockIdx.y * p.M + m) * p.N + n] = val;
+            pbase[(int64_t)(m - pm0) * pld + (n - pn0)] = val;
           } else if constexpr (OUT == kOutBf16) {
             ((uint16_t*)p.out)[(int64_t)m * p.ldo + n] = (uint16_t)f32_to_bf16_rne(val);
           } else {
@@ -375,7 +386,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const int wave = tid >> 6, lane = tid & 63;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, &tm, &tn);
+  const int tile_local = xcd_remap(blockIdx.x, gridDim.x);
+  tile_to_mn(p.tile_base + tile_local, p.tiles_m, p.tiles_n, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kb_begin = blockIdx.y * p.kb_per_split;
   const int kb_end = min(p.kblocks, kb_begin + p.kb_per_split);
@@ -505,10 +517,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   if constexpr (MODE == kTensorwise) tscale = p.ra[0] * p.rb[0];
   // Interior tiles store without per-element checks; edge tiles check rows
   // and columns.
+  float* pbase = nullptr;
+  int64_t pld = 0;
+  int pm0 = 0, pn0 = 0;
+  if constexpr (SPLIT) {
+    if (p.part_tiled) {
+      pbase = p.partial + ((int64_t)blockIdx.y * gridDim.x + tile_local) * (BM * BN);
+      pld = BN;
+      pm0 = m0;
+      pn0 = n0;
+    } else {
+      pbase = p.partial + (int64_t)blockIdx.y * p.M * p.N;
+      pld = p.N;
+    }
+  }
   if (m0 + BM <= p.M && n0 + BN <= p.N)
-    store_acc<false, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, m0 + wm0, n0 + wn0, frow, fhalf);
+    store_acc<false, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, m0 + wm0, n0 + wn0, frow, fhalf,
+                                               pbase, pld, pm0, pn0);
   else
-    store_acc<true, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, m0 + wm0, n0 + wn0, frow, fhalf);
+    store_acc<true, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, m0 + wm0, n0 + wn0, frow, fhalf,
+                                              pbase, pld, pm0, pn0);
 }
 #undef FP8BW_ISSUE
 
@@ -545,6 +573,32 @@ hipError_t launch_zero_bf16(void* out, int64_t rows, int64_t cols, hipStream_t s
   return hipGetLastError();
 }
 
+// Sum tile-local split partials ([split][tile][BM][BN], grouped tile ids
+// tile_base ..) in split order and write the output tiles.
+template <int BM, int BN, int OUT>
+__global__ __launch_bounds__(256) void splitk_reduce_tiled_kernel(
+    const float* __restrict__ part, int splits, int ntiles, int tile_base, int tiles_m,
+    int tiles_n, int M, int N, void* __restrict__ out, int64_t ldo) {
+  const int64_t per_tile = (int64_t)BM * BN;
+  const int64_t total = per_tile * ntiles;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * 256) {
+    const int tl = (int)(idx / per_tile);
+    const int e = (int)(idx - (int64_t)tl * per_tile);
+    const int r = e / BN, c = e - r * BN;
+    int tm, tn;
+    tile_to_mn(tile_base + tl, tiles_m, tiles_n, &tm, &tn);
+    const int m = tm * BM + r, n = tn * BN + c;
+    if (m >= M || n >= N) continue;
+    float s = 0.f;
+    for (int k = 0; k < splits; ++k) s += part[(int64_t)k * total + idx];
+    if (OUT == kOutBf16)
+      ((uint16_t*)out)[(int64_t)m * ldo + n] = (uint16_t)f32_to_bf16_rne(s);
+    else
+      ((float*)out)[(int64_t)m * ldo + n] = s;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Config table.
 struct Cfg {
@@ -574,40 +628,86 @@ bool gemm_config_ok(const GemmProblem& p, int cfg) {
   return true;
 }
 
-size_t gemm_ws_bytes(int64_t M, int64_t N, int splits) {
-  return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+// Compute units of the current device (the number of workgroups that run
+// concurrently with one large-tile workgroup per CU); 256 when unknown.
+static int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
-void gemm_choose(const GemmProblem& p, int* config, int* splits) {
-  const int64_t kblocks = (p.K + 127) / 128;
-  int cfg;
+static int heuristic_config(const GemmProblem& p) {
   const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (p.M >= 256 && p.N >= 256 && t256 >= 128 && gemm_config_ok(p, 3))
-    cfg = 3;
-  else if (p.M >= 256 && p.N >= 128 && gemm_config_ok(p, 2))
-    cfg = 2;
-  else if (p.M >= 128 && p.N >= 128)
-    cfg = 0;
-  else
-    cfg = 1;
-  const int bm = kCfgs[cfg].bm, bn = kCfgs[cfg].bn;
-  const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
-  int s = 1;
-  if (tiles < 256 && kblocks >= 16) {
-    int64_t want = (512 + tiles - 1) / tiles;
-    int64_t maxs = kblocks / 8;
-    s = (int)(want < maxs ? want : maxs);
-    if (s < 1) s = 1;
-    const int64_t per = (kblocks + s - 1) / s;
-    s = (int)((kblocks + per - 1) / per);
+  if (p.M >= 256 && p.N >= 256 && t256 >= 128 && gemm_config_ok(p, 3)) return 3;
+  if (p.M >= 256 && p.N >= 128 && gemm_config_ok(p, 2)) return 2;
+  if (p.M >= 128 && p.N >= 128) return 0;
+  return 1;
+}
+
+GemmPlan gemm_plan(const GemmProblem& p, int config, int splits, bool allow_split) {
+  GemmPlan pl;
+  pl.cfg = config >= 0 ? config : heuristic_config(p);
+  const int bm = kCfgs[pl.cfg].bm, bn = kCfgs[pl.cfg].bn;
+  const int64_t kblocks = (p.K + 127) / 128;
+  pl.tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+  pl.splits = 1;
+  pl.tail_splits = 1;
+  pl.tiles_full = pl.tiles;
+  const int cus = num_cus();
+  if (splits > 0) {
+    pl.splits = splits;
+  } else if (allow_split) {
+    if (pl.tiles < cus && kblocks >= 16) {
+      // Too few tiles to fill the chip: split K over the whole problem.
+      int64_t want = (2 * cus + pl.tiles - 1) / pl.tiles;
+      int64_t maxs = kblocks / 8;
+      int64_t sp = want < maxs ? want : maxs;
+      if (sp < 1) sp = 1;
+      const int64_t per = (kblocks + sp - 1) / sp;
+      pl.splits = (int)((kblocks + per - 1) / per);
+    } else if (kCfgs[pl.cfg].kind == 1 && pl.tiles > cus) {
+      // Full rounds of one tile per CU run unsplit; the leftover tiles of
+      // the last, partial round are split over K across the idle CUs.
+      const int64_t full = pl.tiles / cus * cus, rem = pl.tiles - full;
+      if (rem > 0) {
+        int64_t sp = cus / rem;
+        const int64_t maxs = kblocks / 4;
+        if (sp > maxs) sp = maxs;
+        if (sp >= 2) {
+          const int64_t per = (kblocks + sp - 1) / sp;
+          pl.tail_splits = (int)((kblocks + per - 1) / per);
+          if (pl.tail_splits >= 2) pl.tiles_full = full;
+          else pl.tail_splits = 1;
+        }
+      }
+    }
   }
-  *config = cfg;
-  *splits = s;
+  if (pl.splits > 1)
+    pl.ws_bytes = (size_t)pl.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
+  else if (pl.tail_splits > 1)
+    pl.ws_bytes = (size_t)pl.tail_splits * (size_t)(pl.tiles - pl.tiles_full) * bm * bn * sizeof(float);
+  else
+    pl.ws_bytes = 0;
+  return pl;
 }
 
 template <int BM, int BN, int WGM, int WGN, int STAGES, int MODE>
-static hipError_t launch_v2(const GemmArgs& a, int splits, int out_kind, hipStream_t stream) {
-  dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)splits);
+static hipError_t launch_v2(const GemmArgs& a, int ntiles, int splits, int out_kind,
+                            hipStream_t stream) {
+  dim3 grid((unsigned)ntiles, (unsigned)splits);
   dim3 block(64 * WGM * WGN);
   if (splits > 1)
     hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutF32, true>), grid, block, 0, stream, a);
@@ -619,13 +719,37 @@ static hipError_t launch_v2(const GemmArgs& a, int splits, int out_kind, hipStre
 }
 
 template <int BM, int BN, int WGM, int WGN, int STAGES>
-static hipError_t launch_v2_mode(const GemmArgs& a, int mode, int splits, int out_kind,
-                                 hipStream_t stream) {
+static hipError_t launch_v2_mode(const GemmArgs& a, int mode, int ntiles, int splits,
+                                 int out_kind, hipStream_t stream) {
   switch (mode) {
-    case kBlockB128: return launch_v2<BM, BN, WGM, WGN, STAGES, kBlockB128>(a, splits, out_kind, stream);
-    case kBlockB1x128: return launch_v2<BM, BN, WGM, WGN, STAGES, kBlockB1x128>(a, splits, out_kind, stream);
-    default: return launch_v2<BM, BN, WGM, WGN, STAGES, kTensorwise>(a, splits, out_kind, stream);
+    case kBlockB128: return launch_v2<BM, BN, WGM, WGN, STAGES, kBlockB128>(a, ntiles, splits, out_kind, stream);
+    case kBlockB1x128: return launch_v2<BM, BN, WGM, WGN, STAGES, kBlockB1x128>(a, ntiles, splits, out_kind, stream);
+    default: return launch_v2<BM, BN, WGM, WGN, STAGES, kTensorwise>(a, ntiles, splits, out_kind, stream);
   }
+}
+
+template <int BM, int BN>
+static hipError_t launch_tiled_reduce(const GemmArgs& a, int splits, int ntiles, int out_kind,
+                                      hipStream_t stream) {
+  const int64_t total = (int64_t)BM * BN * ntiles;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (out_kind == kOutBf16)
+    hipLaunchKernelGGL((splitk_reduce_tiled_kernel<BM, BN, kOutBf16>), dim3((unsigned)blocks),
+                       dim3(256), 0, stream, (const float*)a.partial, splits, ntiles, a.tile_base,
+                       a.tiles_m, a.tiles_n, a.M, a.N, a.out, a.ldo);
+  else
+    hipLaunchKernelGGL((splitk_reduce_tiled_kernel<BM, BN, kOutF32>), dim3((unsigned)blocks),
+                       dim3(256), 0, stream, (const float*)a.partial, splits, ntiles, a.tile_base,
+                       a.tiles_m, a.tiles_n, a.M, a.N, a.out, a.ldo);
+  return hipGetLastError();
+}
+
+// One launch of large-tile config `cfg` over grouped tiles [base, base + ntiles).
+static hipError_t launch_v2_cfg(int cfg, const GemmArgs& a, int mode, int ntiles, int splits,
+                                int out_kind, hipStream_t stream) {
+  if (cfg == 2) return launch_v2_mode<256, 128, 2, 2, 3>(a, mode, ntiles, splits, out_kind, stream);
+  return launch_v2_mode<256, 256, 2, 4, 2>(a, mode, ntiles, splits, out_kind, stream);
 }
 
 template <int BM, int BN, int MODE>
@@ -650,8 +774,9 @@ static hipError_t launch_mode(const GemmArgs& a, int mode, int splits, int out_k
   }
 }
 
-hipError_t launch_gemm(const GemmProblem& p, int cfg, int splits, void* ws, hipStream_t stream) {
+hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
+  const int cfg = pl.cfg;
   const int bm = kCfgs[cfg].bm, bn = kCfgs[cfg].bn;
   GemmArgs a;
   a.a = (const uint8_t*)p.a;
@@ -672,15 +797,30 @@ hipError_t launch_gemm(const GemmProblem& p, int cfg, int splits, void* ws, hipS
   a.kblocks = (int)((p.K + 127) / 128);
   a.tiles_m = (int)((p.M + bm - 1) / bm);
   a.tiles_n = (int)((p.N + bn - 1) / bn);
-  if (splits < 1) splits = 1;
-  a.kb_per_split = (a.kblocks + splits - 1) / splits;
-  if (a.kblocks == 0) a.kb_per_split = 0;
+  a.tile_base = 0;
+  a.part_tiled = 0;
+  const int splits = pl.splits < 1 ? 1 : pl.splits;
+  a.kb_per_split = a.kblocks == 0 ? 0 : (a.kblocks + splits - 1) / splits;
   hipError_t e;
-  switch (cfg) {
-    case 0: e = launch_mode<128, 128>(a, p.mode, splits, p.out_kind, stream); break;
-    case 1: e = launch_mode<64, 64>(a, p.mode, splits, p.out_kind, stream); break;
-    case 2: e = launch_v2_mode<256, 128, 2, 2, 3>(a, p.mode, splits, p.out_kind, stream); break;
-    default: e = launch_v2_mode<256, 256, 2, 4, 2>(a, p.mode, splits, p.out_kind, stream); break;
+  if (kCfgs[cfg].kind == 0) {
+    e = cfg == 0 ? launch_mode<128, 128>(a, p.mode, splits, p.out_kind, stream)
+                 : launch_mode<64, 64>(a, p.mode, splits, p.out_kind, stream);
+  } else {
+    // Full rounds (or the whole problem) unsplit or whole-problem split-K.
+    const int nmain = (int)(pl.tail_splits > 1 ? pl.tiles_full : pl.tiles);
+    e = nmain > 0 ? launch_v2_cfg(cfg, a, p.mode, nmain, splits, p.out_kind, stream) : hipSuccess;
+    if (e == hipSuccess && pl.tail_splits > 1) {
+      // Leftover tiles split over K into tile-local partials, then reduced.
+      GemmArgs t = a;
+      const int ntail = (int)(pl.tiles - pl.tiles_full);
+      t.tile_base = (int)pl.tiles_full;
+      t.part_tiled = 1;
+      t.kb_per_split = (a.kblocks + pl.tail_splits - 1) / pl.tail_splits;
+      e = launch_v2_cfg(cfg, t, p.mode, ntail, pl.tail_splits, p.out_kind, stream);
+      if (e == hipSuccess)
+        e = cfg == 2 ? launch_tiled_reduce<256, 128>(t, pl.tail_splits, ntail, p.out_kind, stream)
+                     : launch_tiled_reduce<256, 256>(t, pl.tail_splits, ntail, p.out_kind, stream);
+    }
   }
   if (e != hipSuccess || splits <= 1) return e;
   const int64_t total = p.M * p.N;

@@ -47,13 +47,25 @@ struct GemmProblem {
 
 // Tile configurations; the table lives in gemm.hip.
 int gemm_num_configs();
-// Heuristic choice of (config, split) for a problem.
-void gemm_choose(const GemmProblem& p, int* config, int* splits);
-// Whether config `cfg` accepts this problem (mode support).
+// Whether config `cfg` accepts this problem.
 bool gemm_config_ok(const GemmProblem& p, int cfg);
-// Workspace bytes for a split count (fp32 partials [splits, M, N]).
-size_t gemm_ws_bytes(int64_t M, int64_t N, int splits);
-hipError_t launch_gemm(const GemmProblem& p, int cfg, int splits, void* ws, hipStream_t stream);
+
+// How one GEMM call is run: the tile configuration, a whole-problem split-K
+// count (fp32 partials [splits, M, N], then an ordered reduce), or a tail
+// split (tiles_full tiles unsplit, the remaining tiles split tail_splits
+// ways into tile-local partials, then reduced), and the workspace it needs.
+struct GemmPlan {
+  int cfg;
+  int splits;
+  int tail_splits;
+  int64_t tiles;
+  int64_t tiles_full;
+  size_t ws_bytes;
+};
+// config < 0: built-in choice; splits > 0 forces a whole-problem split
+// (no tail split); splits == 0 lets the plan choose when allow_split.
+GemmPlan gemm_plan(const GemmProblem& p, int config, int splits, bool allow_split);
+hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, void* ws, hipStream_t stream);
 // Fill a contiguous bf16 [rows, cols] matrix with +0.
 hipError_t launch_zero_bf16(void* out, int64_t rows, int64_t cols, hipStream_t stream);
 

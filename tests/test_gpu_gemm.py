@@ -224,3 +224,29 @@ def test_gemm_deterministic(gpu):
     o2 = fp8.fp8_scaled_gemm_blockwise(aq, ar, bq, br, splits=4, config=0, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+
+
+def test_tail_split_of_last_round():
+    """272 tiles of 256x256 on 256 CUs: the leftover 16 tiles (the last
+    row-block of tiles in the grouped order) run split-K into tile-local
+    partials.  Rows of that block and random others match the oracle, and
+    the split and unsplit runs agree within the fp32 rounding bound."""
+    import torch as _t
+    dev = _t.device("cuda", 0)
+    rng = np.random.default_rng(40)
+    M, N, K = 4352, 4096, 2048
+    aq = _random_codes(rng, (M, K))
+    bq = _random_codes(rng, (N, K))
+    ar = rng.uniform(1e-3, 2e-3, (M, K // 128)).astype(np.float32)
+    br = rng.uniform(1e-3, 2e-3, (N // 128, K // 128)).astype(np.float32)
+    args = (_up_codes(aq, dev), _up_scales_colmajor(ar, dev), _up_codes(bq, dev),
+            _up_scales_colmajor(br, dev))
+    say("gemm tail split auto")
+    auto = fp8.fp8_scaled_gemm_blockwise(*args, out_dtype=_t.float32)
+    say("gemm tail split forced off")
+    plain = fp8.fp8_scaled_gemm_blockwise(*args, out_dtype=_t.float32, config=3, splits=1)
+    _t.cuda.synchronize()
+    rows = np.unique(np.r_[np.arange(M - 256, M, 3), rng.choice(M - 256, 32, replace=False)])
+    ref, S = gemm.blockwise_gemm(aq[rows], ar[rows], bq, br, "128x128", with_bound=True)
+    for name, out in (("auto", auto), ("plain", plain)):
+        check_gemm_output(host_f32(out)[rows], ref, S, K // 128, "f32", f"tail split {name}")

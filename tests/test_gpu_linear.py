@@ -60,7 +60,9 @@ def test_linear_llama4_shapes_sampled(gpu, mnk):
     say("llama4 generate", mnk)
     x, w, dy = _inputs(M, N, K, seed=2, device="cuda")
     rng = np.random.default_rng(M + N)
-    rows = np.sort(rng.choice(M, 16, replace=False))
+    # random rows plus rows of the last row-block of tiles (where leftover
+    # tiles of a partial last round are computed split-K)
+    rows = np.unique(np.r_[rng.choice(M, 12, replace=False), M - 1, M - 77, M - 200, M - 256])
     say("llama4 fwd", mnk)
     y = fp8.fp8_linear_fwd(x, w)
     torch.cuda.synchronize()
@@ -86,7 +88,7 @@ def test_linear_llama4_shapes_sampled(gpu, mnk):
     say("llama4 wgrad", mnk)
     dw = fp8.fp8_linear_wgrad(dy, x)
     torch.cuda.synchronize()
-    nrows = np.sort(rng.choice(N, 16, replace=False))
+    nrows = np.unique(np.r_[rng.choice(N, 12, replace=False), N - 1, N - 100, N - 255])
     dycols = _idx(dy, cols=nrows)                  # dY[:, n] -> [M, 16]
     xcols = _idx(x, cols=kcols)                    # X[:, k]  -> [M, 256]
     ref, S = gemm.blockwise_gemm(*quant.quant_1x128_along_rows(dycols),
