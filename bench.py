@@ -135,38 +135,78 @@ def run_gpu(steps, warmup, seed):
             "quant_gbps": qbytes / (qms * 1e-3) / 1e9}
 
 
-def cpu_baseline(seed):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    fwd and dgrad on 64 output rows (each with the full quantized weight) and
-    wgrad on 64 x 1024 outputs (full M contraction).  Inputs drawn on the
-    host with the same recipe (CPU generator stream)."""
+def cpu_baseline(seed, min_seconds=10.0, max_samples=8):
+    """The oracle, as it stands, on a bounded sample of the same workload.
+    One sample: fwd and dgrad on 64 output rows (each with the full quantized
+    weight) and wgrad on 64 x 1024 outputs (full M contraction), inputs drawn
+    on the host with the same recipe.  Fresh samples (new seeds) are run
+    until at least `min_seconds` of oracle time has accumulated (at most
+    `max_samples`), and the rate is total sampled flops / total time."""
     from oracle import linear
     from synth import inputs
     rows, kcols = 64, 1024
     g = inputs.bf16_bits
-    x = g(inputs.randn_bf16((rows, K), seed=inputs.tensor_seed(seed, "x")))
-    w = g(inputs.linear_weight_bf16(N, K, seed=inputs.tensor_seed(seed, "w")))
-    dy = g(inputs.randn_bf16((rows, N), seed=inputs.tensor_seed(seed, "dy")))
-    dy_cols = g(inputs.randn_bf16((M, rows), seed=inputs.tensor_seed(seed + 1, "dy")))
-    x_cols = g(inputs.randn_bf16((M, kcols), seed=inputs.tensor_seed(seed + 1, "x")))
     threads = None
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=None)
     except Exception:
         pass
-    t0 = time.perf_counter()
-    linear.fwd(x, w)
-    linear.dgrad(dy, w)
-    linear.wgrad(dy_cols, x_cols)
-    dt = time.perf_counter() - t0
-    flops = 2 * rows * N * K + 2 * rows * K * N + 2 * rows * kcols * M
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+    flops_one = 2 * rows * N * K + 2 * rows * K * N + 2 * rows * kcols * M
+    total_t, n = 0.0, 0
+    while n < max_samples and (n == 0 or total_t < min_seconds):
+        sd = seed + 1000 * (n + 1)
+        x = g(inputs.randn_bf16((rows, K), seed=inputs.tensor_seed(sd, "x")))
+        w = g(inputs.linear_weight_bf16(N, K, seed=inputs.tensor_seed(sd, "w")))
+        dy = g(inputs.randn_bf16((rows, N), seed=inputs.tensor_seed(sd, "dy")))
+        dy_cols = g(inputs.randn_bf16((M, rows), seed=inputs.tensor_seed(sd + 1, "dy")))
+        x_cols = g(inputs.randn_bf16((M, kcols), seed=inputs.tensor_seed(sd + 1, "x")))
+        t0 = time.perf_counter()
+        linear.fwd(x, w)
+        linear.dgrad(dy, w)
+        linear.wgrad(dy_cols, x_cols)
+        total_t += time.perf_counter() - t0
+        n += 1
+    flops = flops_one * n
+    return {"value": round(flops / total_t / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": (f"oracle (quantize + block-rescaled float64 GEMM) for fwd and dgrad on "
-                       f"{rows} of {M} output rows and wgrad on {rows} x {kcols} of {N} x {K} "
-                       f"outputs, full contraction and full quantization of each operand used; "
-                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s")}
+            "sample": (f"{n} samples, each the oracle (quantize + block-rescaled float64 GEMM) "
+                       f"for fwd and dgrad on {rows} of {M} output rows and wgrad on {rows} x "
+                       f"{kcols} of {N} x {K} outputs (full contraction, full quantization of "
+                       f"each operand used): {flops / 1e9:.1f} GFLOP in {total_t:.1f} s")}
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_fwd_blockwise_M16640_N5120_K8192_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "blockwise_scaled_fp8_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the forward GEMM, from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, valid only while the GEMM source is the
+    one those counters were taken on (sha256 recorded in the summary)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        rec = json.loads(text.split("TRAFFIC_JSON:", 1)[1].strip().splitlines()[0])
+        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("gemm_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_probe(gib):
+    """A plain device-to-device copy of `gib` GiB (one read + one write of
+    each byte), run so that a profiler's FETCH_SIZE / WRITE_SIZE for it can
+    calibrate the same counters on the GEMM."""
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return n
 
 
 def main():
@@ -176,6 +216,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build runs "
@@ -209,15 +251,18 @@ def main():
         "config": {"workload": "fp8 blockwise linear fwd+dgrad+wgrad incl. quantization",
                    "M": M, "N": N, "K": K, "recipes": "fwd/dgrad 1x128 x 128x128, wgrad 1x128 x 1x128",
                    "seed": args.seed},
-        "roofline": {"bound": "mfma", "kernel": "gemm fwd (blockwise, M16640 N5120 K8192)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "fwd blockwise GEMM call M16640 N5120 K8192 (main + tail-split + reduce launches)",
                      "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": measured_traffic()},
         "gemm_tflops": {k: v["tflops"] for k, v in r["kernels"].items() if "tflops" in v},
         "quant_gbps": round(r["quant_gbps"], 1),
         "quant_frac_of_hbm_peak": round(r["quant_gbps"] / HBM_PEAK_GBS, 4),
         "kernels": r["kernels"],
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
     }
+    if args.copy_probe_gib > 0:
+        out["copy_probe_bytes"] = copy_probe(args.copy_probe_gib)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.seed)
     print(json.dumps(out), flush=True)
