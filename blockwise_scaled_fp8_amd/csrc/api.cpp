@@ -122,7 +122,6 @@ FP8BW_API int fp8_blockwise_quant(const void* x, int64_t rows, int64_t cols, int
                 (long long)rs_row, (long long)rs_kb, (long long)ni, (long long)nj);
   hipStream_t s = (hipStream_t)stream;
   if (block == FP8BW_BLOCK_1x128 && !transpose) {
-    if (cdiv(cdiv(cols, 128), 4) > kMaxGridY) return fail(FP8BW_ERR_SHAPE, "too many column blocks");
     return hip_status(fp8bw::launch_quant_1x128_rows(x, rows, cols, ld_x, q, ld_q, recip, rs_row, rs_kb, s),
                       "fp8_blockwise_quant");
   }

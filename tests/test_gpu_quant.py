@@ -61,6 +61,23 @@ def test_quant_1x128_small(gpu, shape):
     _check_1x128(_adversarial(*shape, seed=5), gpu, f"adversarial {shape}")
 
 
+@pytest.mark.parametrize("shape", [(16400, 1152), (8200, 1664)])
+def test_quant_1x128_several_tiles_per_workgroup_sampled(gpu, shape):
+    """Shapes where one workgroup walks several column tiles (odd and even
+    counts, a partial last tile, a partial last band of rows): bit-exact on
+    sampled rows, which the oracle quantizes independently."""
+    rows = np.unique(np.r_[0, 1, 15, 16, shape[0] - 1, shape[0] - 9, shape[0] - 17,
+                           np.random.default_rng(shape[0]).integers(0, shape[0], 40)])
+    for what, x in (("randn", inputs.randn_bf16(shape, seed=inputs.tensor_seed(1, "x"))),
+                    ("adversarial", _adversarial(*shape, seed=5))):
+        say("quant 1x128 sampled", what, shape)
+        q, r = fp8.fp8_blockwise_quant(x.to(gpu), "1x128")
+        torch.cuda.synchronize()
+        oq, orc = quant.quant_1x128(bits(x[torch.from_numpy(rows)]))
+        assert_codes_equal(host_u8(q)[rows], oq, f"{what} {shape}")
+        assert_f32_equal(host_f32(r)[rows], orc, f"{what} {shape}")
+
+
 def _sweep_rows(amax):
     """Rows of 128 bf16 values: each row holds +amax (fixing the block scale
     at 448/amax) followed by 127 consecutive bf16 patterns of magnitude <=
@@ -91,7 +108,8 @@ def test_quant_1x128_square_full(gpu, n):
     _check_1x128(x, gpu, f"square {n}")
 
 
-@pytest.mark.parametrize("shape", [(256, 512), (130, 384), (1, 128), (1024, 1024), (4096, 4096)])
+@pytest.mark.parametrize("shape", [(256, 512), (130, 384), (1, 128), (1024, 1024), (4096, 4096),
+                                   (2600, 8320)])
 def test_quant_128x128(gpu, shape):
     x = inputs.randn_bf16(shape, seed=inputs.tensor_seed(4, "w"))
     _check_128(x, gpu, f"randn {shape}")
@@ -99,7 +117,8 @@ def test_quant_128x128(gpu, shape):
         _check_128(_adversarial(*shape, seed=6), gpu, f"adversarial {shape}")
 
 
-@pytest.mark.parametrize("shape", [(256, 512), (144, 384), (16, 128), (384, 272), (1024, 2048)])
+@pytest.mark.parametrize("shape", [(256, 512), (144, 384), (16, 128), (384, 272), (1024, 2048),
+                                   (2608, 8320)])
 def test_quant_128x128_transposed(gpu, shape):
     x = inputs.linear_weight_bf16(*shape, seed=inputs.tensor_seed(5, "w"))
     _check_128(x, gpu, f"linear-init {shape}", transpose=True)
@@ -107,7 +126,7 @@ def test_quant_128x128_transposed(gpu, shape):
 
 
 @pytest.mark.parametrize("shape", [(256, 64), (128, 80), (272, 48), (384, 208), (1024, 1024),
-                                   (2048, 640)])
+                                   (2048, 640), (16640, 1040), (8320, 2000)])
 def test_quant_1x128_along_rows_transposed(gpu, shape):
     x = inputs.randn_bf16(shape, seed=inputs.tensor_seed(6, "dy"))
     _check_cols_t(x, gpu, f"randn {shape}")
