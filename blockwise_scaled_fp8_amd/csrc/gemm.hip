@@ -82,6 +82,16 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int half)
   return f;
 }
 
+// Fragment read at precomputed byte offsets of its two 16-byte chunks.
+__device__ __forceinline__ v8i load_frag_at(const uint8_t* tile, uint32_t lo, uint32_t hi) {
+  const uint4 a = *(const uint4*)(tile + lo);
+  const uint4 b = *(const uint4*)(tile + hi);
+  v8i f;
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  return f;
+}
+
 template <int BM, int BN, int MODE, int OUT, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -267,6 +277,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// End of a K block: this wave's loads of the next stage have landed (vmcnt
+// <= N) and its LDS reads of the current stage have returned (lgkmcnt 0),
+// then the barrier makes both hold for every wave before any wave issues
+// loads into the stage just read.
+template <int N>
+__device__ __forceinline__ void stage_sync() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+  __builtin_amdgcn_s_barrier();
+}
+
 // Tile order: XCD-aware (the dispatcher deals workgroups round-robin to the
 // 8 XCDs; xcd_remap gives each XCD a contiguous range of tile ids) then
 // grouped (tile_to_mn: GROUP_M row-blocks per column sweep) so that
@@ -377,10 +398,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   static_assert(TN >= 2, "the rescale ring assumes at least two column sub-tiles");
   static_assert(LPS < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t sA[STAGES][BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB[STAGES][BN * 128];
-  __shared__ __attribute__((aligned(16))) float sRa[SCALED ? STAGES : 1][SCALED ? BM : 4];
-  __shared__ __attribute__((aligned(16))) float sRb[SCALED ? STAGES : 1][SCALED ? SBS : 4];
+  // Every stage is an LDS variable of its own and the stage loop below is
+  // unrolled, so each access names its stage statically.  The compiler can
+  // then tell that a stage's fragment reads do not alias the direct loads
+  // in flight into another stage and does not wait for those loads before
+  // the reads; the explicit vmcnt wait + barrier at the end of each K block
+  // orders the loads before the reads of their own stage.
+  constexpr int S3 = STAGES == 3;
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * 128], sA1[BM * 128], sA2[S3 ? BM * 128 : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 128], sB1[BN * 128], sB2[S3 ? BN * 128 : 16];
+  __shared__ __attribute__((aligned(16))) float sRa0[SCALED ? BM : 4], sRa1[SCALED ? BM : 4],
+      sRa2[SCALED && S3 ? BM : 4];
+  __shared__ __attribute__((aligned(16))) float sRb0[SCALED ? SBS : 4], sRb1[SCALED ? SBS : 4],
+      sRb2[SCALED && S3 ? SBS : 4];
+  uint8_t* const sA[3] = {sA0, sA1, sA2};
+  uint8_t* const sB[3] = {sB0, sB1, sB2};
+  float* const sRa[3] = {sRa0, sRa1, sRa2};
+  float* const sRb[3] = {sRb0, sRb1, sRb2};
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -413,9 +447,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   }
 
 #define FP8BW_ISSUE(kb, st)                                                                  \
-  issue_stage<AI, BI, RAI, RBI, RAB, RBB, NW, MODE>(p, (kb), sA[st], sB[st], sRa[SCALED ? (st) : 0], \
-                                                    sRb[SCALED ? (st) : 0], aoff, boff, wave,  \
-                                                    lane, m0, n0)
+  issue_stage<AI, BI, RAI, RBI, RAB, RBB, NW, MODE>(p, (kb), sA[st], sB[st], sRa[st], sRb[st], \
+                                                    aoff, boff, wave, lane, m0, n0)
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -441,19 +474,39 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     }
     __builtin_amdgcn_s_barrier();
   }
-  for (int it = 0; it < nkb; ++it) {
-    const int st = it % STAGES;
-    FP8BW_ISSUE(min(kb_begin + it + STAGES - 1, kb_last), (it + STAGES - 1) % STAGES);
+  for (int it0 = 0; it0 < nkb; it0 += STAGES) {
+#pragma unroll
+  for (int st = 0; st < STAGES; ++st) {
+    const int it = it0 + st;
+    if (it >= nkb) break;
+    FP8BW_ISSUE(min(kb_begin + it + STAGES - 1, kb_last), (st + STAGES - 1) % STAGES);
+
+    // LDS byte offsets of this lane's fragment chunks and scales.  Sub-tile
+    // i of a wave is 16 rows (2 KB) further down and keeps the same swizzle,
+    // so every read is a base offset plus a constant.  The offsets are made
+    // opaque each K block: otherwise the compiler hoists one address per
+    // fragment and stage out of the loop and runs out of registers.
+    uint32_t a_lo = (wm0 + frow) * 128 + (((2 * fhalf) ^ swz(wm0 + frow)) << 4);
+    uint32_t a_hi = (wm0 + frow) * 128 + (((2 * fhalf + 1) ^ swz(wm0 + frow)) << 4);
+    uint32_t b_lo = (wn0 + frow) * 128 + (((2 * fhalf) ^ swz(wn0 + frow)) << 4);
+    uint32_t b_hi = (wn0 + frow) * 128 + (((2 * fhalf + 1) ^ swz(wn0 + frow)) << 4);
+    uint32_t ra_off = (wm0 + 4 * fhalf) * 4;
+    uint32_t rb_off = (wn0 + frow) * 4;
+    asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(ra_off), "+v"(rb_off));
+    const uint8_t* tA = sA[st];
+    const uint8_t* tB = sB[st];
+    const uint8_t* tRa = (const uint8_t*)sRa[st];
+    const uint8_t* tRb = (const uint8_t*)sRb[st];
 
     v8i bf[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bf[j] = load_frag(sB[st], wn0 + 16 * j + frow, fhalf);
+    for (int j = 0; j < TN; ++j) bf[j] = load_frag_at(tB, b_lo + 2048 * j, b_hi + 2048 * j);
     float sbn = 0.f;
     float sbc[TN];
     if constexpr (MODE == kBlockB128) sbn = sRb[st][(n0 + wn0) / 128 - n0 / 128];
     if constexpr (MODE == kBlockB1x128) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sbc[j] = sRb[st][wn0 + 16 * j + frow];
+      for (int j = 0; j < TN; ++j) sbc[j] = *(const float*)(tRb + rb_off + 64 * j);
     }
     // MFMA-granularity pipeline over the TM x TN sub-tiles (row-major): the
     // partial of sub-tile t lands in ring slot t % 3 and is folded into its
@@ -462,9 +515,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     constexpr int T = TM * TN;
     v8i af[2];
     v4f sa[2];
-    af[0] = load_frag(sA[st], wm0 + frow, fhalf);
+    af[0] = load_frag_at(tA, a_lo, a_hi);
     if constexpr (SCALED) {
-      sa[0] = *(const v4f*)&sRa[st][wm0 + 4 * fhalf];
+      sa[0] = *(const v4f*)(tRa + ra_off);
       if constexpr (MODE == kBlockB128) sa[0] = sa[0] * sbn;
     }
     v4f ring[3];
@@ -492,9 +545,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
       // Prefetch row i+1 into the slot of row i-1 only after the last
       // rescale of row i-1 (step i*TN + 1) has read its scales.
       if (t < T && j == 1 && i + 1 < TM) {
-        af[(i + 1) & 1] = load_frag(sA[st], wm0 + 16 * (i + 1) + frow, fhalf);
+        af[(i + 1) & 1] = load_frag_at(tA, a_lo + 2048 * (i + 1), a_hi + 2048 * (i + 1));
         if constexpr (SCALED) {
-          sa[(i + 1) & 1] = *(const v4f*)&sRa[st][wm0 + 16 * (i + 1) + 4 * fhalf];
+          sa[(i + 1) & 1] = *(const v4f*)(tRa + ra_off + 64 * (i + 1));
           if constexpr (MODE == kBlockB128) sa[(i + 1) & 1] = sa[(i + 1) & 1] * sbn;
         }
       }
@@ -506,10 +559,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
       }
     }
     if constexpr (STAGES == 3)
-      wait_vmcnt<LPS>();
+      stage_sync<LPS>();
     else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
+      stage_sync<0>();
+  }
   }
   wait_vmcnt<0>();
 
