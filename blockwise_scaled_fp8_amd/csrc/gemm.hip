@@ -82,6 +82,9 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int half)
   return f;
 }
 
+// How many 16-row A sub-tiles ahead the large-tile kernel reads fragments.
+constexpr int kRowPrefetch = 1;
+
 // Fragment read at precomputed byte offsets of its two 16-byte chunks.
 __device__ __forceinline__ v8i load_frag_at(const uint8_t* tile, uint32_t lo, uint32_t hi) {
   const uint4 a = *(const uint4*)(tile + lo);
@@ -513,22 +516,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     // accumulator two MFMAs later, when it is complete, so each MFMA issues
     // with the previous partials' rescale FMAs in its shadow.
     constexpr int T = TM * TN;
-    v8i af[2];
-    v4f sa[2];
-    af[0] = load_frag_at(tA, a_lo, a_hi);
-    if constexpr (SCALED) {
-      sa[0] = *(const v4f*)(tRa + ra_off);
-      if constexpr (MODE == kBlockB128) sa[0] = sa[0] * sbn;
+    // A rows are read PF rows ahead into a ring of PF + 1 fragment slots:
+    // row i + PF goes into the slot of row i - 1, its fragment as soon as row
+    // i starts (row i - 1's MFMAs are issued) and its scales one step later
+    // (after the last rescale of row i - 1 has read them).
+    constexpr int PF = kRowPrefetch < TM ? kRowPrefetch : TM - 1;
+    constexpr int NS = PF + 1;
+    v8i af[NS];
+    v4f sa[NS];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      af[i] = load_frag_at(tA, a_lo + 2048 * i, a_hi + 2048 * i);
+      if constexpr (SCALED) {
+        sa[i] = *(const v4f*)(tRa + ra_off + 64 * i);
+        if constexpr (MODE == kBlockB128) sa[i] = sa[i] * sbn;
+      }
     }
     v4f ring[3];
 #pragma unroll
     for (int t = 0; t < T + 2; ++t) {
       const int i = t / TN, j = t % TN;
+      if (t < T && j == 0 && i + PF < TM)
+        af[(i + PF) % NS] = load_frag_at(tA, a_lo + 2048 * (i + PF), a_hi + 2048 * (i + PF));
       if (t < T) {
         if (MODE == kTensorwise)
-          acc[i][j] = mfma_fp8(af[i & 1], bf[j], acc[i][j]);
+          acc[i][j] = mfma_fp8(af[i % NS], bf[j], acc[i][j]);
         else
-          ring[t % 3] = mfma_fp8(af[i & 1], bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+          ring[t % 3] = mfma_fp8(af[i % NS], bf[j], v4f{0.f, 0.f, 0.f, 0.f});
       }
       if constexpr (SCALED) {
         if (t >= 2) {
@@ -536,25 +550,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             if constexpr (MODE == kBlockB128)
-              acc[iu][ju][v] = __builtin_fmaf(ring[u % 3][v], sa[iu & 1][v], acc[iu][ju][v]);
+              acc[iu][ju][v] = __builtin_fmaf(ring[u % 3][v], sa[iu % NS][v], acc[iu][ju][v]);
             else
-              acc[iu][ju][v] = __builtin_fmaf(ring[u % 3][v] * sbc[ju], sa[iu & 1][v], acc[iu][ju][v]);
+              acc[iu][ju][v] = __builtin_fmaf(ring[u % 3][v] * sbc[ju], sa[iu % NS][v], acc[iu][ju][v]);
           }
         }
-      }
-      // Prefetch row i+1 into the slot of row i-1 only after the last
-      // rescale of row i-1 (step i*TN + 1) has read its scales.
-      if (t < T && j == 1 && i + 1 < TM) {
-        af[(i + 1) & 1] = load_frag_at(tA, a_lo + 2048 * (i + 1), a_hi + 2048 * (i + 1));
-        if constexpr (SCALED) {
-          sa[(i + 1) & 1] = *(const v4f*)(tRa + ra_off + 64 * (i + 1));
-          if constexpr (MODE == kBlockB128) sa[(i + 1) & 1] = sa[(i + 1) & 1] * sbn;
+        if (t < T && j == 1 && i + PF < TM) {
+          sa[(i + PF) % NS] = *(const v4f*)(tRa + ra_off + 64 * (i + PF));
+          if constexpr (MODE == kBlockB128) sa[(i + PF) % NS] = sa[(i + PF) % NS] * sbn;
         }
       }
-      if constexpr (SCALED) {
+      // 128x128 B blocks: one MFMA, then the 4 rescale FMAs of an earlier
+      // partial.  (For per-row B scales the compiler's own interleave of the
+      // 8 VALU ops per MFMA measured faster.)
+      if constexpr (MODE == kBlockB128) {
         if (t < T) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, MODE == kBlockB1x128 ? 8 : 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
       }
     }
