@@ -16,7 +16,9 @@ Prints one JSON line: `value` is the step's effective throughput,
 3 * 2MNK flops / step time (TFLOP/s); `roofline` is for the dominant kernel,
 the forward blockwise GEMM (2MNK flops per launch / its average duration vs
 the 5.0 PFLOP/s dense FP8 peak); `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.
+bounded sample of the same workload.  Also reported: `fused_quant_step`, the
+same step with each bf16 tensor quantized once into both code layouts, and
+`quant_standalone`, the quantizers alone on a 32768^2 input.
 """
 
 import argparse
@@ -94,13 +96,37 @@ def step_plan(wl):
     ]
 
 
-def run_gpu(steps, warmup, seed):
+def step_plan_dual(wl):
+    """The same step with each bf16 tensor read once: X -> X and X^T codes,
+    W -> W and W^T codes, dY -> dY and dY^T codes (fp8_blockwise_quant_dual,
+    bit-identical outputs), then the three GEMMs."""
+    import blockwise_scaled_fp8_amd as fp8
+    d = fp8.fp8_blockwise_quant_dual
+    g = fp8.fp8_scaled_gemm_blockwise
+    return [
+        ("quant_dual X", lambda: d(wl.x, "1x128", q=wl.xq, recip=wl.xr, qt=wl.xtq, recip_t=wl.xtr),
+         2 * M * K + 2 * M * K + 4 * (M * cdiv(K, 128) + K * cdiv(M, 128)), "B"),
+        ("quant_dual W", lambda: d(wl.w, "128x128", q=wl.wq, recip=wl.wr, qt=wl.wtq, recip_t=wl.wtr),
+         2 * N * K + 2 * N * K + 8 * cdiv(N, 128) * cdiv(K, 128), "B"),
+        ("gemm fwd", lambda: g(wl.xq, wl.xr, wl.wq, wl.wr, "128x128", out=wl.y),
+         2 * M * N * K, "flop"),
+        ("quant_dual dY", lambda: d(wl.dy, "1x128", q=wl.dyq, recip=wl.dyr, qt=wl.dytq, recip_t=wl.dytr),
+         2 * M * N + 2 * M * N + 4 * (M * cdiv(N, 128) + N * cdiv(M, 128)), "B"),
+        ("gemm dgrad", lambda: g(wl.dyq, wl.dyr, wl.wtq, wl.wtr, "128x128", out=wl.dx),
+         2 * M * N * K, "flop"),
+        ("gemm wgrad", lambda: g(wl.dytq, wl.dytr, wl.xtq, wl.xtr, "1x128", out=wl.dw),
+         2 * M * N * K, "flop"),
+    ]
+
+
+def run_gpu(steps, warmup, seed, plan_fn=None, wl=None):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     import blockwise_scaled_fp8_amd as fp8
     fp8.load_library()
-    wl = Workload(seed, dev)
-    plan = step_plan(wl)
+    if wl is None:
+        wl = Workload(seed, dev)
+    plan = (plan_fn or step_plan)(wl)
     torch.cuda.synchronize()
     for _ in range(warmup):
         for _, fn, _, _ in plan:
@@ -132,7 +158,42 @@ def run_gpu(steps, warmup, seed):
     qms = sum(ms for (_, _, _, u), ms in zip(plan, per) if u == "B")
     return {"wall_ms_per_step": wall / steps * 1e3, "gpu_ms_per_step": gpu_ms, "per_ms": per,
             "plan": [(nm, w, u) for nm, _, w, u in plan], "kernels": kernels,
-            "quant_gbps": qbytes / (qms * 1e-3) / 1e9}
+            "quant_gbps": qbytes / (qms * 1e-3) / 1e9, "quant_us": qms * 1e3, "workload": wl}
+
+
+def quant_standalone(seed, size=32768, reps=10):
+    """The quantizers alone on one square bf16 input far larger than the
+    256 MB Infinity Cache (32768^2: 2 GiB in, 1 GiB of codes out), both block
+    shapes, HIP events around each call on the launch stream.  Algorithmic
+    bytes as in the step (2 B read + 1 B written per element + 4 B per
+    scale)."""
+    import blockwise_scaled_fp8_amd as fp8
+    from synth import inputs
+    dev = torch.device("cuda", 0)
+    x = inputs.randn_bf16((size, size), seed=inputs.tensor_seed(seed, "a"), device=dev)
+    q = torch.empty(size, size, dtype=torch.uint8, device=dev)
+    res = {}
+    for block in ("1x128", "128x128"):
+        nkb = cdiv(size, 128)
+        rows = size if block == "1x128" else cdiv(size, 128)
+        recip = torch.empty(nkb, rows, dtype=torch.float32, device=dev).t()
+        for _ in range(3):
+            fp8.fp8_blockwise_quant(x, block, q=q, recip=recip)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record(stream)
+        for i in range(reps):
+            fp8.fp8_blockwise_quant(x, block, q=q, recip=recip)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(reps)) / reps
+        gbps = quant_bytes(size, size, block) / (ms * 1e-3) / 1e9
+        res[block] = {"avg_us": round(ms * 1e3, 1), "gbps": round(gbps, 1),
+                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)}
+    del x, q
+    torch.cuda.empty_cache()
+    return {"shape": [size, size], **res}
 
 
 def cpu_baseline(seed, min_seconds=10.0, max_samples=8):
@@ -216,6 +277,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quant-standalone", action="store_true",
+                    help="skip the standalone 32768^2 quantizer timing")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -261,6 +324,17 @@ def main():
         "kernels": r["kernels"],
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
     }
+    rd = run_gpu(args.steps, args.warmup, args.seed, plan_fn=step_plan_dual, wl=r["workload"])
+    out["fused_quant_step"] = {
+        "note": "same step, each bf16 tensor quantized once into both layouts",
+        "ms_per_step": round(rd["gpu_ms_per_step"], 4),
+        "value": round(flops / (rd["gpu_ms_per_step"] * 1e-3) / 1e12, 1),
+        "quant_us_per_step": round(rd["quant_us"], 1),
+        "quant_gbps": round(rd["quant_gbps"], 1),
+        "kernels": rd["kernels"]}
+    del r, rd
+    if not args.no_quant_standalone:
+        out["quant_standalone"] = quant_standalone(args.seed)
     if args.copy_probe_gib > 0:
         out["copy_probe_bytes"] = copy_probe(args.copy_probe_gib)
     if not args.no_cpu_baseline:

@@ -10,6 +10,7 @@ from ._lib import FP8BWError, PROTOTYPES, load_library, lib_path  # noqa: F401
 from .ops import (  # noqa: F401
     colmajor_empty,
     fp8_blockwise_quant,
+    fp8_blockwise_quant_dual,
     fp8_linear_dgrad,
     fp8_linear_fwd,
     fp8_linear_wgrad,

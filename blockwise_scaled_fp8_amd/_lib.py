@@ -20,6 +20,8 @@ PROTOTYPES = {
     "fp8bw_last_error": (ctypes.c_char_p, []),
     "fp8_blockwise_quant": (c_int, [c_ptr, c_i64, c_i64, c_i64, c_int, c_int, c_ptr, c_i64,
                                     c_ptr, c_i64, c_i64, c_ptr]),
+    "fp8_blockwise_quant_dual": (c_int, [c_ptr, c_i64, c_i64, c_i64, c_int, c_ptr, c_i64, c_ptr,
+                                         c_i64, c_i64, c_ptr, c_i64, c_ptr, c_i64, c_i64, c_ptr]),
     "fp8bw_tensorwise_quant_ws_bytes": (c_size, [c_i64, c_i64]),
     "fp8_tensorwise_quant": (c_int, [c_ptr, c_i64, c_i64, c_i64, c_ptr, c_i64, c_ptr, c_ptr,
                                      c_size, c_ptr]),

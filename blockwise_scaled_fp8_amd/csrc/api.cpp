@@ -96,16 +96,18 @@ static int check_quant_common(const void* x, int64_t rows, int64_t cols, int64_t
   return FP8BW_OK;
 }
 
-FP8BW_API int fp8_blockwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
-                                  int block, int transpose, void* q, int64_t ld_q, float* recip,
-                                  int64_t rs_row, int64_t rs_kb, void* stream) {
+// Validation of one quantizer output (codes q and scales recip) for a block
+// kind and orientation.
+static int check_quant_output(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int block,
+                              int transpose, void* q, int64_t ld_q, float* recip, int64_t rs_row,
+                              int64_t rs_kb) {
   if (block != FP8BW_BLOCK_1x128 && block != FP8BW_BLOCK_128x128)
     return fail(FP8BW_ERR_UNSUPPORTED, "unknown block kind %d", block);
   if (transpose != 0 && transpose != 1) return fail(FP8BW_ERR_UNSUPPORTED, "transpose must be 0 or 1");
   if (transpose && rows % 16) return fail(FP8BW_ERR_SHAPE, "transpose=1 needs rows %% 16 == 0 (rows=%lld)", (long long)rows);
   int st = check_quant_common(x, rows, cols, ld_x, q, ld_q, transpose ? rows : cols);
   if (st != FP8BW_OK) return st;
-  if (rows == 0 || cols == 0) return ok();
+  if (rows == 0 || cols == 0) return FP8BW_OK;
   if (!recip) return fail(FP8BW_ERR_NULL, "recip must be non-null");
   if (!aligned(recip, 4)) return fail(FP8BW_ERR_ALIGN, "recip must be 4-byte aligned");
   // Scale grid [ni, nj] in (output row or row block, output column block).
@@ -120,17 +122,46 @@ FP8BW_API int fp8_blockwise_quant(const void* x, int64_t rows, int64_t cols, int
   if (!strides_injective(ni, nj, rs_row, rs_kb))
     return fail(FP8BW_ERR_LAYOUT, "recip strides (%lld, %lld) alias or are negative for a %lldx%lld scale grid",
                 (long long)rs_row, (long long)rs_kb, (long long)ni, (long long)nj);
+  if ((transpose || block == FP8BW_BLOCK_128x128) && cdiv(rows, 128) > kMaxGridY)
+    return fail(FP8BW_ERR_SHAPE, "too many row blocks");
+  return FP8BW_OK;
+}
+
+FP8BW_API int fp8_blockwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  int block, int transpose, void* q, int64_t ld_q, float* recip,
+                                  int64_t rs_row, int64_t rs_kb, void* stream) {
+  int st = check_quant_output(x, rows, cols, ld_x, block, transpose, q, ld_q, recip, rs_row, rs_kb);
+  if (st != FP8BW_OK) return st;
+  if (rows == 0 || cols == 0) return ok();
   hipStream_t s = (hipStream_t)stream;
-  if (block == FP8BW_BLOCK_1x128 && !transpose) {
+  if (block == FP8BW_BLOCK_1x128 && !transpose)
     return hip_status(fp8bw::launch_quant_1x128_rows(x, rows, cols, ld_x, q, ld_q, recip, rs_row, rs_kb, s),
                       "fp8_blockwise_quant");
-  }
-  if (cdiv(rows, 128) > kMaxGridY) return fail(FP8BW_ERR_SHAPE, "too many row blocks");
   if (block == FP8BW_BLOCK_1x128)
     return hip_status(fp8bw::launch_quant_1x128_cols_t(x, rows, cols, ld_x, q, ld_q, recip, rs_row, rs_kb, s),
                       "fp8_blockwise_quant");
   return hip_status(fp8bw::launch_quant_128x128(x, rows, cols, ld_x, transpose, q, ld_q, recip, rs_row, rs_kb, s),
                     "fp8_blockwise_quant");
+}
+
+FP8BW_API int fp8_blockwise_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                       int block, void* q, int64_t ld_q, float* recip,
+                                       int64_t rs_row, int64_t rs_kb, void* qt, int64_t ld_qt,
+                                       float* recip_t, int64_t rst_row, int64_t rst_kb,
+                                       void* stream) {
+  int st = check_quant_output(x, rows, cols, ld_x, block, 0, q, ld_q, recip, rs_row, rs_kb);
+  if (st != FP8BW_OK) return st;
+  st = check_quant_output(x, rows, cols, ld_x, block, 1, qt, ld_qt, recip_t, rst_row, rst_kb);
+  if (st != FP8BW_OK) return st;
+  if (rows == 0 || cols == 0) return ok();
+  // The two code buffers must not overlap (scales are the caller's to keep apart).
+  const uintptr_t q0 = (uintptr_t)q, q1 = q0 + (uintptr_t)((rows - 1) * ld_q + cols);
+  const uintptr_t t0 = (uintptr_t)qt, t1 = t0 + (uintptr_t)((cols - 1) * ld_qt + rows);
+  if (q0 < t1 && t0 < q1) return fail(FP8BW_ERR_LAYOUT, "q and qt overlap");
+  return hip_status(fp8bw::launch_quant_dual(x, rows, cols, ld_x, block == FP8BW_BLOCK_128x128, q, ld_q,
+                                             recip, rs_row, rs_kb, qt, ld_qt, recip_t, rst_row, rst_kb,
+                                             (hipStream_t)stream),
+                    "fp8_blockwise_quant_dual");
 }
 
 FP8BW_API size_t fp8bw_tensorwise_quant_ws_bytes(int64_t rows, int64_t cols) {

@@ -24,6 +24,14 @@ hipError_t launch_quant_128x128(const void* x, int64_t rows, int64_t cols, int64
 hipError_t launch_quant_1x128_cols_t(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
                                      void* q, int64_t ld_q, float* recip, int64_t rs_row,
                                      int64_t rs_kb, hipStream_t stream);
+// Both layouts from one read: block_128 = 0 writes the 1x128 row-block codes
+// (q, recip[r*rs_row + kb*rs_kb]) and the transposed 1x128 column-block codes
+// (qt = x^T, recip_t[c*rst_row + mb*rst_kb]); block_128 = 1 writes the
+// 128x128 codes and the transposed codes with the tile scale in both orders.
+hipError_t launch_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int block_128,
+                             void* q, int64_t ld_q, float* recip, int64_t rs_row, int64_t rs_kb,
+                             void* qt, int64_t ld_qt, float* recip_t, int64_t rst_row,
+                             int64_t rst_kb, hipStream_t stream);
 // Per-tensor: partial amax into ws (n_partials floats), then quantize.
 int tensorwise_partials(int64_t rows, int64_t cols);
 hipError_t launch_quant_tensorwise(const void* x, int64_t rows, int64_t cols, int64_t ld_x,

@@ -111,16 +111,38 @@ hipError_t launch_quant_1x128_rows(const void* x, int64_t rows, int64_t cols, in
 // 16 column groups of a store over the banks and keeps every 16-byte group
 // of 4 dwords intact.  The tile is then read back as 16-byte segments of
 // output rows, 8 lanes per 128-byte row.
-enum TileMode { kTileScale = 0, kTileScaleT = 1, kColScaleT = 2 };
+// Dual outputs from one read of the tile: W and W^T codes with the one tile
+// scale (written in both index orders), or the 1x128 row blocks (a row's 128
+// columns of the tile are one block; its 16 threads are one DPP row) and the
+// transposed 1x128 column blocks of X or dY together.
+enum TileMode {
+  kTileScale = 0,       // codes as they are, tile scale
+  kTileScaleT = 1,      // transposed codes, tile scale
+  kColScaleT = 2,       // transposed codes, one scale per column per 128 rows
+  kTileScaleBoth = 3,   // both code layouts, tile scale
+  kRowColBoth = 4       // codes with 1x128 row scales + transposed codes with column scales
+};
+
+struct TileOut {
+  uint8_t* q;           // codes as they are [rows, cols] (ld_q)
+  int64_t ld_q;
+  float* recip;         // their scales (rs_row, rs_kb)
+  int64_t rs_row, rs_kb;
+  uint8_t* qt;          // transposed codes [cols, rows] (ld_qt)
+  int64_t ld_qt;
+  float* recip_t;       // their scales (rst_row, rst_kb)
+  int64_t rst_row, rst_kb;
+};
 
 template <int MODE>
 __global__ __launch_bounds__(256) void quant_tile_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
-    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ recip, int64_t rs_row,
-    int64_t rs_kb) {
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld_x, const TileOut o) {
+  constexpr bool PLAIN = MODE == kTileScale || MODE == kTileScaleBoth || MODE == kRowColBoth;
   constexpr bool T = MODE != kTileScale;
-  __shared__ float red[4][MODE == kColScaleT ? 128 : 1];
-  __shared__ float ssc[MODE == kColScaleT ? 128 : 1];
+  constexpr bool COLS = MODE == kColScaleT || MODE == kRowColBoth;
+  constexpr bool ROWS = MODE == kRowColBoth;
+  __shared__ float red[4][COLS ? 128 : 1];
+  __shared__ float ssc[COLS ? 128 : 1];
   __shared__ __attribute__((aligned(16))) uint32_t tile[T ? 128 * 32 : 4];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -143,7 +165,7 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(
   }
 
   float s = 0.f;
-  if constexpr (MODE != kColScaleT) {
+  if constexpr (!COLS) {
     float m = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) m = fmaxf(m, absmax8(v[k]));
@@ -152,10 +174,8 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(
     __syncthreads();
     s = scale_from_amax(fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0])));
     if (tid == 0) {
-      if (T)
-        recip[cb * rs_row + rb * rs_kb] = recip_of_scale(s);
-      else
-        recip[rb * rs_row + cb * rs_kb] = recip_of_scale(s);
+      if (PLAIN) o.recip[rb * o.rs_row + cb * o.rs_kb] = recip_of_scale(s);
+      if (T) o.recip_t[cb * o.rst_row + rb * o.rst_kb] = recip_of_scale(s);
     }
   } else {
 #pragma unroll
@@ -172,23 +192,31 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(
       const float a = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
       const float sc = scale_from_amax(a);
       ssc[tid] = sc;
-      if (cb * 128 + tid < cols) recip[(cb * 128 + tid) * rs_row + rb * rs_kb] = recip_of_scale(sc);
+      if (cb * 128 + tid < cols)
+        o.recip_t[(cb * 128 + tid) * o.rst_row + rb * o.rst_kb] = recip_of_scale(sc);
     }
     __syncthreads();
   }
 
-  if constexpr (!T) {
+  if constexpr (PLAIN) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int64_t r = rb * 128 + 64 * (k >> 2) + 4 * j + (k & 3);
-      const uint2 code = quant8(v[k], s);
-      if (col_in && r < rows) *(uint2*)(q + r * ld_q + col) = code;
+      float sr = s;
+      if constexpr (ROWS) {
+        // 1x128 row block: this row's 128 columns live in this DPP row
+        sr = scale_from_amax(row16_max(absmax8(v[k])));
+        if (g == 0 && r < rows) o.recip[r * o.rs_row + cb * o.rs_kb] = recip_of_scale(sr);
+      }
+      const uint2 code = quant8(v[k], sr);
+      if (col_in && r < rows) *(uint2*)(o.q + r * o.ld_q + col) = code;
     }
-  } else {
+  }
+  if constexpr (T) {
     const int sw = 4 * (g & 7);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float sc = MODE == kColScaleT ? ssc[8 * g + c] : s;
+      const float sc = COLS ? ssc[8 * g + c] : s;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const uint32_t w = cvt4_e4m3(bf16_elem(v[4 * p + 0], c) * sc, bf16_elem(v[4 * p + 1], c) * sc,
@@ -203,33 +231,49 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(
       const int oc = id >> 3, seg = id & 7;       // output row in the tile, 16-row segment
       const uint4 val = *(const uint4*)&tile[oc * 32 + ((4 * seg) ^ (4 * ((oc >> 3) & 7)))];
       const int64_t orow = cb * 128 + oc, ocol = rb * 128 + 16 * seg;
-      if (orow < cols && ocol < rows) *(uint4*)(q + orow * ld_q + ocol) = val;
+      if (orow < cols && ocol < rows) *(uint4*)(o.qt + orow * o.ld_qt + ocol) = val;
     }
   }
 }
 
 template <int MODE>
-static hipError_t launch_tile(const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* q,
-                              int64_t ld_q, float* recip, int64_t rs_row, int64_t rs_kb,
-                              hipStream_t stream) {
+static hipError_t launch_tile(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                              const TileOut& o, hipStream_t stream) {
   if (rows == 0 || cols == 0) return hipSuccess;
   const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
   hipLaunchKernelGGL(quant_tile_kernel<MODE>, grid, dim3(256), 0, stream, (const uint16_t*)x, rows,
-                     cols, ld_x, (uint8_t*)q, ld_q, recip, rs_row, rs_kb);
+                     cols, ld_x, o);
   return hipGetLastError();
+}
+
+static TileOut plain_out(void* q, int64_t ld_q, float* recip, int64_t rs_row, int64_t rs_kb) {
+  return TileOut{(uint8_t*)q, ld_q, recip, rs_row, rs_kb, nullptr, 0, nullptr, 0, 0};
+}
+static TileOut trans_out(void* q, int64_t ld_q, float* recip, int64_t rs_row, int64_t rs_kb) {
+  return TileOut{nullptr, 0, nullptr, 0, 0, (uint8_t*)q, ld_q, recip, rs_row, rs_kb};
 }
 
 hipError_t launch_quant_128x128(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
                                 int transpose, void* q, int64_t ld_q, float* recip,
                                 int64_t rs_row, int64_t rs_kb, hipStream_t stream) {
-  return transpose ? launch_tile<kTileScaleT>(x, rows, cols, ld_x, q, ld_q, recip, rs_row, rs_kb, stream)
-                   : launch_tile<kTileScale>(x, rows, cols, ld_x, q, ld_q, recip, rs_row, rs_kb, stream);
+  return transpose
+             ? launch_tile<kTileScaleT>(x, rows, cols, ld_x, trans_out(q, ld_q, recip, rs_row, rs_kb), stream)
+             : launch_tile<kTileScale>(x, rows, cols, ld_x, plain_out(q, ld_q, recip, rs_row, rs_kb), stream);
 }
 
 hipError_t launch_quant_1x128_cols_t(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
                                      void* q, int64_t ld_q, float* recip, int64_t rs_row,
                                      int64_t rs_kb, hipStream_t stream) {
-  return launch_tile<kColScaleT>(x, rows, cols, ld_x, q, ld_q, recip, rs_row, rs_kb, stream);
+  return launch_tile<kColScaleT>(x, rows, cols, ld_x, trans_out(q, ld_q, recip, rs_row, rs_kb), stream);
+}
+
+hipError_t launch_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int block_128,
+                             void* q, int64_t ld_q, float* recip, int64_t rs_row, int64_t rs_kb,
+                             void* qt, int64_t ld_qt, float* recip_t, int64_t rst_row,
+                             int64_t rst_kb, hipStream_t stream) {
+  const TileOut o{(uint8_t*)q, ld_q, recip, rs_row, rs_kb, (uint8_t*)qt, ld_qt, recip_t, rst_row, rst_kb};
+  return block_128 ? launch_tile<kTileScaleBoth>(x, rows, cols, ld_x, o, stream)
+                   : launch_tile<kRowColBoth>(x, rows, cols, ld_x, o, stream);
 }
 
 // ---------------------------------------------------------------------------

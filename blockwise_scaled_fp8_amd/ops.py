@@ -81,6 +81,38 @@ def fp8_blockwise_quant(x, block="1x128", transpose=False, q=None, recip=None):
     return q, recip
 
 
+def fp8_blockwise_quant_dual(x, block="1x128", q=None, recip=None, qt=None, recip_t=None):
+    """Both layouts from one read of x: returns (q, recip, qt, recip_t), equal
+    to fp8_blockwise_quant(x, block) and fp8_blockwise_quant(x, block,
+    transpose=True)."""
+    lib = load_library()
+    _need_cuda(x)
+    _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    _check_shape(q, (rows, cols), "q")
+    _check_shape(qt, (cols, rows), "qt")
+    ni, nj = scale_grid(rows, cols, block, False)
+    ti, tj = scale_grid(rows, cols, block, True)
+    if recip is None:
+        recip = colmajor_empty(ni, nj, x.device)
+    if recip_t is None:
+        recip_t = colmajor_empty(ti, tj, x.device)
+    _check_shape(recip, (ni, nj), "recip")
+    _check_shape(recip_t, (ti, tj), "recip_t")
+    check(lib.fp8_blockwise_quant_dual(x.data_ptr(), rows, cols, x.stride(0), BLOCKS[block],
+                                       q.data_ptr(), q.stride(0), recip.data_ptr(), recip.stride(0),
+                                       recip.stride(1), qt.data_ptr(), qt.stride(0),
+                                       recip_t.data_ptr(), recip_t.stride(0), recip_t.stride(1),
+                                       _stream(x)))
+    return q, recip, qt, recip_t
+
+
 def fp8_tensorwise_quant(x, q=None, recip=None):
     """Per-tensor quantization: (q uint8 like x, recip fp32 [1] on device)."""
     lib = load_library()

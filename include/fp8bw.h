@@ -109,6 +109,30 @@ int fp8_blockwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
                         int64_t rs_kb, void* stream);
 
 /*
+ * fp8_blockwise_quant_dual -- both layouts from one read of x: the same
+ * codes and scales as fp8_blockwise_quant with transpose=0 into (q, recip)
+ * and with transpose=1 into (qt, recip_t), for a training step that needs
+ * X and X^T (or dY and dY^T, or W and W^T) and would otherwise read the
+ * bf16 tensor twice; the quantizers are the part of the fp8 linear step
+ * the pages single out as slow ([INTEG] Benchmarks).
+ *
+ *   block    FP8BW_BLOCK_1x128: q = 1x128 blocks along the columns with
+ *            recip[r*rs_row + kb*rs_kb]; qt = x^T with 1x128 blocks along
+ *            the rows, recip_t[c*rst_row + mb*rst_kb].
+ *            FP8BW_BLOCK_128x128: q = tile-scaled codes, recip[rb*rs_row +
+ *            cb*rs_kb]; qt = their transpose, recip_t[cb*rst_row +
+ *            rb*rst_kb] (the same values in the other index order).
+ *   q, qt    device E4M3 [rows, cols] (ld_q >= cols) and [cols, rows]
+ *            (ld_qt >= rows); the two must not overlap (checked).
+ *   Requires cols % 16 == 0 and rows % 16 == 0; each output is validated as
+ *   in fp8_blockwise_quant, and results are bit-identical to two calls of it.
+ */
+int fp8_blockwise_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int block,
+                             void* q, int64_t ld_q, float* recip, int64_t rs_row, int64_t rs_kb,
+                             void* qt, int64_t ld_qt, float* recip_t, int64_t rst_row,
+                             int64_t rst_kb, void* stream);
+
+/*
  * fp8_tensorwise_quant -- one scale for the whole tensor ([AITER]
  * per_tensor_quant: the scale returned is the dequant multiplier).
  *   x [rows, cols] bf16 (ld_x), q [rows, cols] E4M3 (ld_q), recip: one

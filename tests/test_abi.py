@@ -73,6 +73,30 @@ def test_quant_validation(lib):
     assert _quant(lib, cols=0, x=None, q=None, recip=None) == OK
 
 
+def _dual(lib, **kw):
+    a = dict(x=P, rows=64, cols=256, ld_x=256, block=0, q=P, ld_q=256, recip=P, rs_row=1,
+             rs_kb=64, qt=P + (1 << 20), ld_qt=64, recip_t=P, rst_row=1, rst_kb=256, stream=None)
+    a.update(kw)
+    return lib.fp8_blockwise_quant_dual(*[a[k] for k in (
+        "x", "rows", "cols", "ld_x", "block", "q", "ld_q", "recip", "rs_row", "rs_kb", "qt",
+        "ld_qt", "recip_t", "rst_row", "rst_kb", "stream")])
+
+
+def test_dual_quant_validation(lib):
+    """Both outputs are validated as fp8_blockwise_quant validates each
+    orientation; the two code buffers may not overlap."""
+    assert _dual(lib, block=2) == UNSUP
+    assert _dual(lib, rows=100, rs_kb=128) == SHAPE      # transposed output needs rows % 16
+    assert _dual(lib, cols=200) == SHAPE
+    assert _dual(lib, qt=None) == NULL
+    assert _dual(lib, recip_t=None) == NULL
+    assert _dual(lib, ld_qt=32) == LAYOUT                # qt rows hold `rows` codes
+    assert _dual(lib, rows=256, rs_kb=256, ld_qt=256, rst_kb=8) == LAYOUT  # transposed scales alias
+    assert _dual(lib, qt=P + 4096) == LAYOUT             # overlaps q
+    assert "overlap" in lib.fp8bw_last_error().decode()
+    assert _dual(lib, rows=0, x=None, q=None, qt=None, recip=None, recip_t=None) == OK
+
+
 def _gemm(lib, fn="fp8_scaled_gemm_blockwise", **kw):
     a = dict(a=P, lda=256, ra=P, ra_s_row=1, ra_s_kb=64, b=P, ldb=256, rb=P, rb_s_row=1,
              rb_s_kb=1, b_block=1, M=64, N=128, K=256, out=P, ldo=128, out_dtype=0, ws=P,

@@ -134,6 +134,36 @@ def test_quant_1x128_along_rows_transposed(gpu, shape):
     _check_cols_t(xt, gpu, f"adversarial {shape}")
 
 
+@pytest.mark.parametrize("block,shape", [("1x128", (256, 512)), ("1x128", (144, 384)),
+                                         ("1x128", (272, 48)), ("1x128", (1040, 2000)),
+                                         ("128x128", (256, 512)), ("128x128", (144, 384)),
+                                         ("128x128", (2608, 1040))])
+def test_quant_dual_layouts(gpu, block, shape):
+    """One read, both layouts: each output bit-exact against the oracle's
+    quantizer for that layout, and equal to the single-layout kernels."""
+    for what, x in (("randn", inputs.randn_bf16(shape, seed=inputs.tensor_seed(12, "x"))),
+                    ("adversarial", _adversarial(*shape, seed=13))):
+        say("quant dual", block, what, shape)
+        xd = x.to(gpu)
+        q, r, qt, rt = fp8.fp8_blockwise_quant_dual(xd, block)
+        q1, r1 = fp8.fp8_blockwise_quant(xd, block)
+        q2, r2 = fp8.fp8_blockwise_quant(xd, block, transpose=True)
+        torch.cuda.synchronize()
+        if block == "1x128":
+            oq, orc = quant.quant_1x128(bits(x))
+            oqt, ort = quant.quant_1x128_along_rows(bits(x))
+        else:
+            oq, orc = quant.quant_128x128(bits(x))
+            oqt, ort = quant.quant_128x128_transposed(bits(x))
+        assert_codes_equal(host_u8(q), oq, f"dual {block} {what} {shape} codes")
+        assert_f32_equal(host_f32(r), orc, f"dual {block} {what} {shape} recip")
+        assert_codes_equal(host_u8(qt), oqt, f"dual {block} {what} {shape} codes^T")
+        assert_f32_equal(host_f32(rt), ort, f"dual {block} {what} {shape} recip^T")
+        assert torch.equal(q, q1) and torch.equal(qt, q2)
+        assert torch.equal(r.view(torch.int32), r1.view(torch.int32))
+        assert torch.equal(rt.view(torch.int32), r2.view(torch.int32))
+
+
 @pytest.mark.parametrize("shape", [(16, 32), (32, 32), (256, 1024), (4096, 1024), (3, 48)])
 def test_quant_tensorwise(gpu, shape):
     x = inputs.randn_bf16(shape, seed=inputs.tensor_seed(7, "x"))
