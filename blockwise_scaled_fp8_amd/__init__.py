@@ -21,3 +21,4 @@ from .ops import (  # noqa: F401
     linear_workspace,
     scale_grid,
 )
+from .torch_ops import Float8BlockwiseLinear  # noqa: E402,F401  (registers torch.ops.fp8bw.*)

@@ -1,0 +1,152 @@
+"""PyTorch integration of the FP8 blockwise linear: custom ops, autograd and
+an nn.Linear counterpart.
+
+The layer above the hot path in the pages' design is a linear module whose
+forward and backward quantize and run the blockwise-scaled GEMM
+(pytorch/ao PR "integrate torch._scaled_mm into Float8BlockwiseLinear and
+add bench script", Summary).  Here that is:
+
+  * three custom ops, ``torch.ops.fp8bw.linear_fwd`` / ``linear_dgrad`` /
+    ``linear_wgrad``, each one call of the C ABI (quantizers + GEMM all run
+    in libfp8bw.so) with a fake (meta) implementation, so ``torch.compile``
+    can trace through them without running them;
+  * ``torch.ops.fp8bw.linear``, the forward op with autograd registered:
+    its backward calls the dgrad and wgrad ops, each with the recipe the
+    pages use for that GEMM (dY 1x128 x W^T 128x128; dY^T 1x128 x X^T 1x128
+    along the token axis);
+  * ``Float8BlockwiseLinear``, a module with ``nn.Linear``'s interface
+    (bias-free) that flattens leading dimensions into the token axis.
+
+Shapes follow the ABI's rules: in_features and out_features multiples of
+128 (they are contraction axes in fwd and dgrad) and a token count that is a
+multiple of 128 when the weight gradient is needed (its contraction axis).
+Everything is bf16.  There is no fallback: without libfp8bw.so the ops raise.
+"""
+
+import math
+
+import torch
+
+from . import ops
+
+
+def _check_2d_bf16(*ts):
+    for t in ts:
+        if t.dim() != 2 or t.dtype != torch.bfloat16:
+            raise ValueError("fp8bw linear ops take 2-D bf16 tensors")
+
+
+@torch.library.custom_op("fp8bw::linear_fwd", mutates_args=())
+def linear_fwd(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """Y[M, N] = X[M, K] . W[N, K]^T, X 1x128 and W 128x128 blocks."""
+    _check_2d_bf16(x, w)
+    return ops.fp8_linear_fwd(x.contiguous(), w.contiguous())
+
+
+@linear_fwd.register_fake
+def _linear_fwd_fake(x, w):
+    _check_2d_bf16(x, w)
+    return x.new_empty((x.shape[0], w.shape[0]))
+
+
+@torch.library.custom_op("fp8bw::linear_dgrad", mutates_args=())
+def linear_dgrad(dy: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """dX[M, K] = dY[M, N] . W[N, K], dY 1x128 and W^T 128x128 blocks."""
+    _check_2d_bf16(dy, w)
+    return ops.fp8_linear_dgrad(dy.contiguous(), w.contiguous())
+
+
+@linear_dgrad.register_fake
+def _linear_dgrad_fake(dy, w):
+    _check_2d_bf16(dy, w)
+    return dy.new_empty((dy.shape[0], w.shape[1]))
+
+
+@torch.library.custom_op("fp8bw::linear_wgrad", mutates_args=())
+def linear_wgrad(dy: torch.Tensor, x: torch.Tensor) -> torch.Tensor:
+    """dW[N, K] = dY[M, N]^T . X[M, K], both 1x128 blocks along M."""
+    _check_2d_bf16(dy, x)
+    return ops.fp8_linear_wgrad(dy.contiguous(), x.contiguous())
+
+
+@linear_wgrad.register_fake
+def _linear_wgrad_fake(dy, x):
+    _check_2d_bf16(dy, x)
+    return dy.new_empty((dy.shape[1], x.shape[1]))
+
+
+@torch.library.custom_op("fp8bw::linear", mutates_args=())
+def linear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """Differentiable FP8 blockwise linear: Y = X . W^T (see linear_fwd)."""
+    _check_2d_bf16(x, w)
+    return ops.fp8_linear_fwd(x.contiguous(), w.contiguous())
+
+
+@linear.register_fake
+def _linear_fake(x, w):
+    _check_2d_bf16(x, w)
+    return x.new_empty((x.shape[0], w.shape[0]))
+
+
+def _linear_setup_context(ctx, inputs, output):
+    x, w = inputs
+    ctx.save_for_backward(x, w)
+
+
+def _linear_backward(ctx, dy):
+    x, w = ctx.saved_tensors
+    dy = dy.contiguous()
+    dx = torch.ops.fp8bw.linear_dgrad(dy, w) if ctx.needs_input_grad[0] else None
+    dw = torch.ops.fp8bw.linear_wgrad(dy, x) if ctx.needs_input_grad[1] else None
+    return dx, dw
+
+
+torch.library.register_autograd("fp8bw::linear", _linear_backward,
+                                setup_context=_linear_setup_context)
+
+
+class Float8BlockwiseLinear(torch.nn.Module):
+    """Bias-free ``nn.Linear`` counterpart whose forward and backward run the
+    FP8 blockwise recipe: y = x W^T with x quantized per 1x128 and W per
+    128x128 block; dX and dW as in ``torch.ops.fp8bw.linear``.
+
+    The weight is a bf16 parameter [out_features, in_features] initialized
+    as ``nn.Linear`` does (U(+-1/sqrt(in_features))).  Inputs [..., in_features]
+    are flattened to [tokens, in_features]."""
+
+    def __init__(self, in_features, out_features, bias=False, device=None, dtype=torch.bfloat16):
+        super().__init__()
+        if bias:
+            raise NotImplementedError("Float8BlockwiseLinear is bias-free")
+        if dtype != torch.bfloat16:
+            raise ValueError("Float8BlockwiseLinear keeps a bf16 weight")
+        if in_features % 128 or out_features % 128:
+            raise ValueError("in_features and out_features must be multiples of 128")
+        self.in_features = in_features
+        self.out_features = out_features
+        self.weight = torch.nn.Parameter(
+            torch.empty(out_features, in_features, device=device, dtype=dtype))
+        self.reset_parameters()
+
+    def reset_parameters(self):
+        bound = 1.0 / math.sqrt(self.in_features)
+        with torch.no_grad():
+            self.weight.uniform_(-bound, bound)
+
+    @classmethod
+    def from_linear(cls, lin):
+        """The same layer from a bias-free ``nn.Linear`` (weight cast to bf16)."""
+        if lin.bias is not None:
+            raise NotImplementedError("Float8BlockwiseLinear is bias-free")
+        m = cls(lin.in_features, lin.out_features, device=lin.weight.device)
+        with torch.no_grad():
+            m.weight.copy_(lin.weight.to(torch.bfloat16))
+        return m
+
+    def forward(self, x):
+        lead = x.shape[:-1]
+        y = torch.ops.fp8bw.linear(x.reshape(-1, self.in_features), self.weight)
+        return y.reshape(*lead, self.out_features)
+
+    def extra_repr(self):
+        return f"in_features={self.in_features}, out_features={self.out_features}, bias=False"

@@ -1,0 +1,66 @@
+"""The PyTorch integration layer without a GPU: op registration, fake (meta)
+shape propagation through forward, autograd and torch.compile tracing, the
+module's interface, and that real CPU tensors are refused (no fallback)."""
+
+import pytest
+import torch
+
+import blockwise_scaled_fp8_amd as fp8
+
+
+def _meta(*shape, grad=False):
+    return torch.empty(*shape, dtype=torch.bfloat16, device="meta", requires_grad=grad)
+
+
+def test_ops_registered():
+    for name in ("linear", "linear_fwd", "linear_dgrad", "linear_wgrad"):
+        assert hasattr(torch.ops.fp8bw, name)
+
+
+def test_fake_shapes():
+    x, w, dy = _meta(256, 512), _meta(384, 512), _meta(256, 384)
+    assert torch.ops.fp8bw.linear_fwd(x, w).shape == (256, 384)
+    assert torch.ops.fp8bw.linear(x, w).shape == (256, 384)
+    assert torch.ops.fp8bw.linear_dgrad(dy, w).shape == (256, 512)
+    assert torch.ops.fp8bw.linear_wgrad(dy, x).shape == (384, 512)
+    with pytest.raises(ValueError):
+        torch.ops.fp8bw.linear_fwd(x.float(), w)
+
+
+def test_module_autograd_shapes_on_meta():
+    m = fp8.Float8BlockwiseLinear(512, 384, device="meta")
+    assert m.weight.shape == (384, 512) and m.weight.dtype == torch.bfloat16
+    x = _meta(2, 128, 512, grad=True)
+    y = m(x)
+    assert y.shape == (2, 128, 384)
+    y.sum().backward()
+    assert x.grad.shape == x.shape and m.weight.grad.shape == m.weight.shape
+
+
+def test_compile_traces_the_custom_ops():
+    """AOT autograd (no code generation) traces forward and backward through
+    the fake implementations in one graph."""
+    m = fp8.Float8BlockwiseLinear(256, 128, device="meta")
+    cm = torch.compile(m, backend="aot_eager", fullgraph=True)
+    x = _meta(128, 256, grad=True)
+    y = cm(x)
+    y.sum().backward()
+    assert y.shape == (128, 128) and x.grad.shape == (128, 256)
+
+
+def test_module_interface():
+    with pytest.raises(NotImplementedError):
+        fp8.Float8BlockwiseLinear(128, 128, bias=True)
+    with pytest.raises(ValueError):
+        fp8.Float8BlockwiseLinear(100, 128)
+    lin = torch.nn.Linear(256, 128, bias=False)
+    m = fp8.Float8BlockwiseLinear.from_linear(lin)
+    assert torch.equal(m.weight, lin.weight.detach().to(torch.bfloat16))
+    bound = 1 / 256 ** 0.5
+    assert float(fp8.Float8BlockwiseLinear(256, 128).weight.abs().max()) <= bound
+
+
+def test_cpu_tensors_are_refused():
+    m = fp8.Float8BlockwiseLinear(128, 128)
+    with pytest.raises(ValueError, match="CUDA"):
+        m(torch.zeros(128, 128, dtype=torch.bfloat16))
