@@ -211,7 +211,8 @@ static int gemm_blockwise_impl(const void* a, int64_t lda, const float* ra, int6
                                int64_t ra_s_kb, const void* b, int64_t ldb, const float* rb,
                                int64_t rb_s_row, int64_t rb_s_kb, int b_block, int64_t M,
                                int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype,
-                               int config, int splits, void* ws, size_t ws_bytes, void* stream) {
+                               int config, int splits, void* ws, size_t ws_bytes, void* stream,
+                               const void* bias = nullptr) {
   if (b_block != FP8BW_BLOCK_1x128 && b_block != FP8BW_BLOCK_128x128)
     return fail(FP8BW_ERR_UNSUPPORTED, "unknown b_block %d", b_block);
   int st = check_gemm_operands(a, lda, b, ldb, M, N, K, out, ldo, out_dtype);
@@ -239,6 +240,7 @@ static int gemm_blockwise_impl(const void* a, int64_t lda, const float* ra, int6
   p.out = out; p.ldo = ldo; p.M = M; p.N = N; p.K = K;
   p.mode = b_block == FP8BW_BLOCK_128x128 ? fp8bw::kBlockB128 : fp8bw::kBlockB1x128;
   p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
+  p.bias = bias;
   if (config >= 0 && !fp8bw::gemm_config_ok(p, config))
     return fail(FP8BW_ERR_UNSUPPORTED, "config %d does not support this problem", config);
   if (splits > kMaxGridY || (kb > 0 && splits > kb) || (kb == 0 && splits > 1))
@@ -304,10 +306,28 @@ FP8BW_API int fp8_scaled_gemm_blockwise_cfg(const void* a, int64_t lda, const fl
                              M, N, K, out, ldo, out_dtype, config, splits, ws, ws_bytes, stream);
 }
 
-FP8BW_API int fp8_scaled_gemm_tensorwise(const void* a, int64_t lda, const float* ra,
-                                         const void* b, int64_t ldb, const float* rb, int64_t M,
-                                         int64_t N, int64_t K, void* out, int64_t ldo,
-                                         int out_dtype, void* stream) {
+static int check_bias(const void* bias) {
+  if (bias && !aligned(bias, 2)) return fail(FP8BW_ERR_ALIGN, "bias must be 2-byte aligned");
+  return FP8BW_OK;
+}
+
+FP8BW_API int fp8_scaled_gemm_blockwise_bias(const void* a, int64_t lda, const float* ra,
+                                             int64_t ra_s_row, int64_t ra_s_kb, const void* b,
+                                             int64_t ldb, const float* rb, int64_t rb_s_row,
+                                             int64_t rb_s_kb, int b_block, int64_t M, int64_t N,
+                                             int64_t K, const void* bias, void* out, int64_t ldo,
+                                             int out_dtype, void* ws, size_t ws_bytes,
+                                             void* stream) {
+  int st = check_bias(bias);
+  if (st != FP8BW_OK) return st;
+  return gemm_blockwise_impl(a, lda, ra, ra_s_row, ra_s_kb, b, ldb, rb, rb_s_row, rb_s_kb, b_block,
+                             M, N, K, out, ldo, out_dtype, -1, 0, ws, ws_bytes, stream, bias);
+}
+
+static int gemm_tensorwise_impl(const void* a, int64_t lda, const float* ra, const void* b,
+                                int64_t ldb, const float* rb, int64_t M, int64_t N, int64_t K,
+                                void* out, int64_t ldo, int out_dtype, void* stream,
+                                const void* bias) {
   int st = check_gemm_operands(a, lda, b, ldb, M, N, K, out, ldo, out_dtype);
   if (st != FP8BW_OK) return st;
   if (K % 16) return fail(FP8BW_ERR_SHAPE, "tensorwise GEMM needs K %% 16 == 0 (K=%lld)", (long long)K);
@@ -320,9 +340,27 @@ FP8BW_API int fp8_scaled_gemm_tensorwise(const void* a, int64_t lda, const float
   p.out = out; p.ldo = ldo; p.M = M; p.N = N; p.K = K;
   p.mode = fp8bw::kTensorwise;
   p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
+  p.bias = bias;
   // No workspace argument: never split.
   const fp8bw::GemmPlan plan = fp8bw::gemm_plan(p, -1, 0, false);
   return hip_status(fp8bw::launch_gemm(p, plan, nullptr, (hipStream_t)stream), "fp8_scaled_gemm_tensorwise");
+}
+
+FP8BW_API int fp8_scaled_gemm_tensorwise(const void* a, int64_t lda, const float* ra,
+                                         const void* b, int64_t ldb, const float* rb, int64_t M,
+                                         int64_t N, int64_t K, void* out, int64_t ldo,
+                                         int out_dtype, void* stream) {
+  return gemm_tensorwise_impl(a, lda, ra, b, ldb, rb, M, N, K, out, ldo, out_dtype, stream, nullptr);
+}
+
+FP8BW_API int fp8_scaled_gemm_tensorwise_bias(const void* a, int64_t lda, const float* ra,
+                                              const void* b, int64_t ldb, const float* rb,
+                                              int64_t M, int64_t N, int64_t K, const void* bias,
+                                              void* out, int64_t ldo, int out_dtype,
+                                              void* stream) {
+  int st = check_bias(bias);
+  if (st != FP8BW_OK) return st;
+  return gemm_tensorwise_impl(a, lda, ra, b, ldb, rb, M, N, K, out, ldo, out_dtype, stream, bias);
 }
 
 // ---------------------------------------------------------------------------

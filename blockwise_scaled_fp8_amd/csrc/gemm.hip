@@ -53,7 +53,14 @@ struct GemmArgs {
   // [split][M][N].
   int tile_base;
   int part_tiled;
+  // Optional bf16 bias [N], added to each output row after scaling and before
+  // the output cast; nullptr for none.  Split-K adds it in the reduce.
+  const uint16_t* bias;
 };
+
+__device__ __forceinline__ float bias_at(const uint16_t* bias, int n) {
+  return bias ? bf16lo(bias[n]) : 0.f;
+}
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
   // Scale operands 0 select the unscaled V_MFMA_F32_16X16X128_F8F6F4;
@@ -246,6 +253,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
         if (m < p.M && n < p.N) {
           float val = acc[i][j][v];
           if (MODE == kTensorwise) val *= tscale;
+          if (!SPLIT) val += bias_at(p.bias, n);
           if (SPLIT) {
             p.partial[((int64_t)blockIdx.y * p.M + m) * p.N + n] = val;
           } else if (OUT == kOutBf16) {
@@ -369,6 +377,7 @@ __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM
         if (!GUARD || (m < p.M && n < p.N)) {
           float val = acc[i][j][v];
           if constexpr (MODE == kTensorwise) val *= tscale;
+          if constexpr (!SPLIT) val += bias_at(p.bias, n);
           if constexpr (SPLIT) {
             pbase[(int64_t)(m - pm0) * pld + (n - pn0)] = val;
           } else if constexpr (OUT == kOutBf16) {
@@ -610,13 +619,15 @@ template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int splits, int M, int N,
                                                             void* __restrict__ out,
-                                                            int64_t ldo) {
+                                                            int64_t ldo,
+                                                            const uint16_t* __restrict__ bias) {
   const int64_t total = (int64_t)M * N;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * 256) {
     float s = 0.f;
     for (int k = 0; k < splits; ++k) s += part[(int64_t)k * total + idx];
     const int64_t m = idx / N, n = idx - m * N;
+    s += bias_at(bias, (int)n);
     if (OUT == kOutBf16)
       ((uint16_t*)out)[m * ldo + n] = (uint16_t)f32_to_bf16_rne(s);
     else
@@ -643,7 +654,8 @@ hipError_t launch_zero_bf16(void* out, int64_t rows, int64_t cols, hipStream_t s
 template <int BM, int BN, int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_tiled_kernel(
     const float* __restrict__ part, int splits, int ntiles, int tile_base, int tiles_m,
-    int tiles_n, int M, int N, void* __restrict__ out, int64_t ldo) {
+    int tiles_n, int M, int N, void* __restrict__ out, int64_t ldo,
+    const uint16_t* __restrict__ bias) {
   const int64_t per_tile = (int64_t)BM * BN;
   const int64_t total = per_tile * ntiles;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
@@ -657,6 +669,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_tiled_kernel(
     if (m >= M || n >= N) continue;
     float s = 0.f;
     for (int k = 0; k < splits; ++k) s += part[(int64_t)k * total + idx];
+    s += bias_at(bias, n);
     if (OUT == kOutBf16)
       ((uint16_t*)out)[(int64_t)m * ldo + n] = (uint16_t)f32_to_bf16_rne(s);
     else
@@ -802,11 +815,11 @@ static hipError_t launch_tiled_reduce(const GemmArgs& a, int splits, int ntiles,
   if (out_kind == kOutBf16)
     hipLaunchKernelGGL((splitk_reduce_tiled_kernel<BM, BN, kOutBf16>), dim3((unsigned)blocks),
                        dim3(256), 0, stream, (const float*)a.partial, splits, ntiles, a.tile_base,
-                       a.tiles_m, a.tiles_n, a.M, a.N, a.out, a.ldo);
+                       a.tiles_m, a.tiles_n, a.M, a.N, a.out, a.ldo, a.bias);
   else
     hipLaunchKernelGGL((splitk_reduce_tiled_kernel<BM, BN, kOutF32>), dim3((unsigned)blocks),
                        dim3(256), 0, stream, (const float*)a.partial, splits, ntiles, a.tile_base,
-                       a.tiles_m, a.tiles_n, a.M, a.N, a.out, a.ldo);
+                       a.tiles_m, a.tiles_n, a.M, a.N, a.out, a.ldo, a.bias);
   return hipGetLastError();
 }
 
@@ -864,6 +877,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
   a.tiles_n = (int)((p.N + bn - 1) / bn);
   a.tile_base = 0;
   a.part_tiled = 0;
+  a.bias = (const uint16_t*)p.bias;
   const int splits = pl.splits < 1 ? 1 : pl.splits;
   a.kb_per_split = a.kblocks == 0 ? 0 : (a.kblocks + splits - 1) / splits;
   hipError_t e;
@@ -893,10 +907,12 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
   if (blocks > 4096) blocks = 4096;
   if (p.out_kind == kOutBf16)
     hipLaunchKernelGGL(splitk_reduce_kernel<kOutBf16>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, (const float*)ws, splits, (int)p.M, (int)p.N, p.out, p.ldo);
+                       stream, (const float*)ws, splits, (int)p.M, (int)p.N, p.out, p.ldo,
+                       (const uint16_t*)p.bias);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<kOutF32>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, (const float*)ws, splits, (int)p.M, (int)p.N, p.out, p.ldo);
+                       stream, (const float*)ws, splits, (int)p.M, (int)p.N, p.out, p.ldo,
+                       (const uint16_t*)p.bias);
   return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@ struct GemmProblem {
   int64_t M, N, K;
   int mode;       // ScaleMode
   int out_kind;   // OutKind
+  const void* bias = nullptr;   // optional bf16 [N] added before the output cast
 };
 
 // Tile configurations; the table lives in gemm.hip.

@@ -130,8 +130,17 @@ def fp8_tensorwise_quant(x, q=None, recip=None):
     return q, recip
 
 
+def _check_bias(bias, N, device):
+    if bias is None:
+        return
+    if bias.dtype != torch.bfloat16 or bias.dim() != 1 or bias.shape[0] != N or bias.stride(0) != 1:
+        raise ValueError(f"bias must be a contiguous bf16 [{N}] tensor")
+    if bias.device != device:
+        raise ValueError("bias must be on the GEMM's device")
+
+
 def fp8_scaled_gemm_blockwise(a, ra, b, rb, b_block="128x128", out_dtype=torch.bfloat16,
-                              out=None, config=None, splits=None):
+                              out=None, config=None, splits=None, bias=None):
     """out[M, N] = blockwise-scaled A . B^T (see include/fp8bw.h).
 
     a uint8 [M, K], ra fp32 [M, K/128] (column-major), b uint8 [N, K], rb fp32
@@ -153,6 +162,15 @@ def fp8_scaled_gemm_blockwise(a, ra, b, rb, b_block="128x128", out_dtype=torch.b
     args = (a.data_ptr(), a.stride(0), ra.data_ptr(), ra.stride(0), ra.stride(1),
             b.data_ptr(), b.stride(0), rb.data_ptr(), rb.stride(0), rb.stride(1),
             BLOCKS[b_block], M, N, K, out.data_ptr(), out.stride(0), OUT_DTYPES[out.dtype])
+    _check_bias(bias, N, a.device)
+    if bias is not None:
+        if config is not None or splits is not None:
+            raise ValueError("bias is not combined with a forced config/splits")
+        nws = lib.fp8bw_gemm_blockwise_ws_bytes(M, N, K)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=a.device)
+        check(lib.fp8_scaled_gemm_blockwise_bias(*args[:14], bias.data_ptr(), *args[14:],
+                                                 ws.data_ptr(), nws, _stream(a)))
+        return out
     if config is None and splits is None:
         nws = lib.fp8bw_gemm_blockwise_ws_bytes(M, N, K)
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=a.device)
@@ -173,7 +191,7 @@ def fp8bw_gemm_num_configs():
     return load_library().fp8bw_gemm_num_configs()
 
 
-def fp8_scaled_gemm_tensorwise(a, ra, b, rb, out_dtype=torch.bfloat16, out=None):
+def fp8_scaled_gemm_tensorwise(a, ra, b, rb, out_dtype=torch.bfloat16, out=None, bias=None):
     """out[M, N] = (A . B^T) * ra * rb with one-element device scales."""
     lib = load_library()
     _need_cuda(a, b, ra, rb)
@@ -187,6 +205,13 @@ def fp8_scaled_gemm_tensorwise(a, ra, b, rb, out_dtype=torch.bfloat16, out=None)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _check_shape(out, (M, N), "out")
+    _check_bias(bias, N, a.device)
+    if bias is not None:
+        check(lib.fp8_scaled_gemm_tensorwise_bias(a.data_ptr(), a.stride(0), ra.data_ptr(),
+                                                  b.data_ptr(), b.stride(0), rb.data_ptr(), M, N, K,
+                                                  bias.data_ptr(), out.data_ptr(), out.stride(0),
+                                                  OUT_DTYPES[out.dtype], _stream(a)))
+        return out
     check(lib.fp8_scaled_gemm_tensorwise(a.data_ptr(), a.stride(0), ra.data_ptr(), b.data_ptr(),
                                          b.stride(0), rb.data_ptr(), M, N, K, out.data_ptr(),
                                          out.stride(0), OUT_DTYPES[out.dtype], _stream(a)))

@@ -198,6 +198,35 @@ int fp8_scaled_gemm_tensorwise(const void* a, int64_t lda, const float* ra, cons
                                void* out, int64_t ldo, int out_dtype, void* stream);
 
 /*
+ * fp8_scaled_gemm_blockwise_bias / fp8_scaled_gemm_tensorwise_bias -- the
+ * same GEMMs with a bias epilogue.  Both GEMM interfaces on the pages take
+ * an optional bias (aiter gemm_a8w8 and torch._scaled_mm, [AITER] Steps to
+ * Reproduce; the inductor tests parametrize has_bias, [INDUCT] Describe the
+ * bug); the pages pass None and do not define its arithmetic.  Here:
+ *
+ *   out[m, n] = cast(acc[m, n] + bias[n])
+ *
+ * where acc is the fp32 result the call without bias would cast (after the
+ * per-tensor scaling for the tensorwise GEMM), the bias value is widened
+ * from bf16 exactly, the add is one fp32 add, and cast is RNE to bf16 or
+ * none for fp32 out.  With split-K the add happens once, in the reduce.
+ *
+ *   bias   device bf16 [N], contiguous, 2-byte aligned; NULL = no bias
+ *          (then identical to the call without _bias).
+ *   Every other argument, status and workspace rule is that of the call
+ *   without _bias.
+ */
+int fp8_scaled_gemm_blockwise_bias(const void* a, int64_t lda, const float* ra, int64_t ra_s_row,
+                                   int64_t ra_s_kb, const void* b, int64_t ldb, const float* rb,
+                                   int64_t rb_s_row, int64_t rb_s_kb, int b_block, int64_t M,
+                                   int64_t N, int64_t K, const void* bias, void* out, int64_t ldo,
+                                   int out_dtype, void* ws, size_t ws_bytes, void* stream);
+int fp8_scaled_gemm_tensorwise_bias(const void* a, int64_t lda, const float* ra, const void* b,
+                                    int64_t ldb, const float* rb, int64_t M, int64_t N, int64_t K,
+                                    const void* bias, void* out, int64_t ldo, int out_dtype,
+                                    void* stream);
+
+/*
  * FP8 blockwise linear layer, fwd / dgrad / wgrad ([INTEG] Summary:
  * Float8BlockwiseLinear; [REPRO] review comments: 1x128 x 128x128 on the
  * grad path, 1x128 x 1x128 for the weight gradient).  All tensors are

@@ -120,6 +120,20 @@ def tensorwise_bound(a_codes, ra, b_codes, rb):
     return (A @ B.T) * abs(float(np.float32(ra)) * float(np.float32(rb)))
 
 
+def add_bias(ref, bias_bits):
+    """Bias epilogue: out[m, n] = ref[m, n] + bias[n], the bf16 bias widened
+    exactly, in float64.  Both GEMM interfaces on the pages take an optional
+    bias ([AITER] Steps to Reproduce: gemm_a8w8 and torch._scaled_mm, passed
+    as None; [INDUCT] Describe the bug: has_bias parametrizes the tests) and
+    define no arithmetic for it; this is the plain reading: added per output
+    column after scaling, before the output cast."""
+    b = e4m3.bf16_bits_to_f32(bias_bits).astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if b.shape != (ref.shape[1],):
+        raise ValueError("bias needs one value per output column")
+    return ref + b[None, :]
+
+
 def fp32_reference(x_bits, w_bits):
     """The unquantized product X . W^T of the bf16 inputs, accumulated in
     float64 ([REPRO] What Changed: the "FP32 reference matmul").  Used as the

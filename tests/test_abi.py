@@ -135,6 +135,22 @@ def test_gemm_validation(lib):
     assert _gemm(lib, "fp8_scaled_gemm_blockwise_cfg", splits=2, ws=None) == WS
 
 
+def test_bias_entry_points_validate(lib):
+    """The _bias entry points share the GEMMs' validation and add a 2-byte
+    alignment check on the bias pointer."""
+    a = dict(a=P, lda=256, ra=P, ra_s_row=1, ra_s_kb=64, b=P, ldb=256, rb=P, rb_s_row=1,
+             rb_s_kb=1, b_block=1, M=64, N=128, K=256)
+    args = [a[k] for k in ("a", "lda", "ra", "ra_s_row", "ra_s_kb", "b", "ldb", "rb", "rb_s_row",
+                           "rb_s_kb", "b_block", "M", "N", "K")]
+    assert lib.fp8_scaled_gemm_blockwise_bias(*args, P + 1, P, 128, 0, P, 1 << 20, None) == ALIGN
+    assert lib.fp8_scaled_gemm_blockwise_bias(*args[:13], 200, P, P, 128, 0, P, 1 << 20,
+                                              None) == SHAPE       # K % 128
+    assert lib.fp8_scaled_gemm_tensorwise_bias(P, 256, P, P, 256, P, 64, 128, 256, P + 1, P, 128,
+                                               0, None) == ALIGN
+    assert lib.fp8_scaled_gemm_tensorwise_bias(P, 256, P, P, 256, P, 64, 128, 200, P, P, 128,
+                                               0, None) == SHAPE   # K % 16
+
+
 def test_tensorwise_validation(lib):
     f = lib.fp8_scaled_gemm_tensorwise
     assert f(P, 32, P, P, 32, P, 16, 32, 24, P, 32, 1, None) == SHAPE        # K % 16

@@ -250,3 +250,62 @@ def test_tail_split_of_last_round():
     ref, S = gemm.blockwise_gemm(aq[rows], ar[rows], bq, br, "128x128", with_bound=True)
     for name, out in (("auto", auto), ("plain", plain)):
         check_gemm_output(host_f32(out)[rows], ref, S, K // 128, "f32", f"tail split {name}")
+
+
+@pytest.mark.parametrize("mnk,b_block,od", [
+    ((128, 256, 512), "128x128", "bf16"),      # small-tile kernel
+    ((77, 130, 384), "1x128", "f32"),          # ragged edges
+    ((256, 256, 16384), "128x128", "f32"),     # whole-problem split-K: bias in the reduce
+    ((2048, 2048, 1024), "128x128", "bf16"),   # large-tile kernel
+    ((4352, 4096, 2048), "128x128", "f32"),    # full rounds + tail split (tiled reduce)
+])
+def test_blockwise_bias_epilogue(gpu, mnk, b_block, od):
+    """out = acc + bias[n] before the cast, on every store path the built-in
+    plan takes (direct stores, whole-problem split-K, tail split); sampled
+    rows against oracle add_bias(ref64, bias) with S + |bias| as the bound."""
+    M, N, K = mnk
+    rng = np.random.default_rng(M + N + K)
+    aq, bq = _random_codes(rng, (M, K)), _random_codes(rng, (N, K))
+    ar = rng.uniform(1e-3, 2e-3, (M, K // 128)).astype(np.float32)
+    nb = N if b_block == "1x128" else -(-N // 128)
+    br = rng.uniform(1e-3, 2e-3, (nb, K // 128)).astype(np.float32)
+    bias = e4m3.f32_to_bf16_bits(rng.normal(0, 4, N).astype(np.float32))
+    dt = torch.bfloat16 if od == "bf16" else torch.float32
+    say("gemm blockwise bias", mnk, b_block, od)
+    bias_d = torch.from_numpy(bias.view(np.int16)).view(torch.bfloat16).to(gpu)
+    out = fp8.fp8_scaled_gemm_blockwise(_up_codes(aq, gpu), _up_scales_colmajor(ar, gpu),
+                                        _up_codes(bq, gpu), _up_scales_colmajor(br, gpu),
+                                        b_block=b_block, out_dtype=dt, bias=bias_d)
+    nob = fp8.fp8_scaled_gemm_blockwise(_up_codes(aq, gpu), _up_scales_colmajor(ar, gpu),
+                                        _up_codes(bq, gpu), _up_scales_colmajor(br, gpu),
+                                        b_block=b_block, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, M - 1, rng.integers(0, M, 24)])
+    ref, S = gemm.blockwise_gemm(aq[rows], ar[rows], bq, br, b_block, with_bound=True)
+    refb = gemm.add_bias(ref, bias)
+    Sb = S + np.abs(e4m3.bf16_bits_to_f32(bias).astype(np.float64))[None, :]
+    check_gemm_output(host_f32(out)[rows], refb, Sb, K // 128, od, f"bias {mnk}")
+    if od == "f32":
+        # the bias is one fp32 add on the unbiased fp32 result
+        expect = host_f32(nob) + e4m3.bf16_bits_to_f32(bias)[None, :]
+        assert np.array_equal(host_f32(out), expect.astype(np.float32))
+
+
+@pytest.mark.parametrize("mnk,od", [((256, 4096, 1024), "bf16"), ((16, 32, 32), "f32")])
+def test_tensorwise_bias_epilogue(gpu, mnk, od):
+    M, N, K = mnk
+    x = bits(inputs.randn_bf16((M, K), seed=inputs.tensor_seed(33, "x")))
+    w = bits(inputs.randn_bf16((N, K), seed=inputs.tensor_seed(33, "w")))
+    xq, xr = quant.quant_tensorwise(x)
+    wq, wr = quant.quant_tensorwise(w)
+    bias = e4m3.f32_to_bf16_bits(np.random.default_rng(N).normal(0, 8, N).astype(np.float32))
+    dt = torch.bfloat16 if od == "bf16" else torch.float32
+    say("gemm tensorwise bias", mnk, od)
+    out = fp8.fp8_scaled_gemm_tensorwise(
+        _up_codes(xq, gpu), torch.tensor([xr], device=gpu), _up_codes(wq, gpu),
+        torch.tensor([wr], device=gpu), out_dtype=dt,
+        bias=torch.from_numpy(bias.view(np.int16)).view(torch.bfloat16).to(gpu))
+    torch.cuda.synchronize()
+    ref = gemm.add_bias(gemm.tensorwise_gemm(xq, xr, wq, wr), bias)
+    S = gemm.tensorwise_bound(xq, xr, wq, wr) + np.abs(e4m3.bf16_bits_to_f32(bias))[None, :]
+    check_gemm_output(host_f32(out), ref, S, -(-K // 128), od, f"tensorwise bias {mnk}")

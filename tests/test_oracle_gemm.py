@@ -209,3 +209,32 @@ def test_linear_compositions():
     wq, wr = quant.quant_128x128(w)
     alt = gemm.blockwise_gemm(dq, dr, np.ascontiguousarray(wq.T), np.ascontiguousarray(wr.T), "128x128")
     assert np.array_equal(alt, linear.dgrad(dy, w))
+
+
+def test_bias_epilogue_against_fraction_and_invariants():
+    """add_bias: the exact rational of (block-rescaled sum + bias[n]) per
+    element on a non-square case (a bias indexed by row instead of column,
+    or dropped, fails), the zero bias is the identity, and a bias of the wrong
+    length is refused."""
+    rng = np.random.default_rng(7)
+    M, N, K = 3, 5, 256
+    a = _random_codes(rng, (M, K))
+    b = _random_codes(rng, (N, K))
+    ra = rng.uniform(0.5, 2, (M, 2)).astype(np.float32)
+    rb = rng.uniform(0.5, 2, (1, 2)).astype(np.float32)
+    bias = e4m3.f32_to_bf16_bits(rng.normal(0, 100, N).astype(np.float32))
+    ref = gemm.blockwise_gemm(a, ra, b, rb, "128x128")
+    out = gemm.add_bias(ref, bias)
+    table = exact.e4m3_table()
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for kb in range(2):
+                p = sum(table[int(a[m, k])] * table[int(b[n, k])]
+                        for k in range(kb * 128, (kb + 1) * 128))
+                tot += p * exact.f32_frac(ra[m, kb]) * exact.f32_frac(rb[0, kb])
+            tot += Fraction(float(e4m3.bf16_bits_to_f32(bias[n])))
+            assert abs(Fraction(out[m, n]) - tot) <= abs(tot) * Fraction(2) ** -50 + Fraction(2) ** -60
+    assert np.array_equal(gemm.add_bias(ref, np.zeros(N, np.uint16)), ref)
+    with pytest.raises(ValueError):
+        gemm.add_bias(ref, bias[:M])
