@@ -17,8 +17,9 @@ Prints one JSON line: `value` is the step's effective throughput,
 the forward blockwise GEMM (2MNK flops per launch / its average duration vs
 the 5.0 PFLOP/s dense FP8 peak); `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload.  Also reported: `fused_quant_step`, the
-same step with each bf16 tensor quantized once into both code layouts, and
-`quant_standalone`, the quantizers alone on a 32768^2 input.
+same step with each bf16 tensor quantized once into both code layouts,
+`grouped_gemm`, the mixture-of-experts grouped GEMM at the forward shape,
+and `quant_standalone`, the quantizers alone on a 32768^2 input.
 """
 
 import argparse
@@ -196,6 +197,40 @@ def quant_standalone(seed, size=32768, reps=10):
     return {"shape": [size, size], **res}
 
 
+def grouped_gemm(seed, wl, groups=8, reps=10):
+    """The grouped (mixture-of-experts) blockwise GEMM at the forward shape:
+    the M = 16640 quantized tokens of X split over `groups` experts with
+    seeded multinomial sizes, one 128x128-quantized N x K weight per expert;
+    2MNK flops in total, timed with HIP events like the step."""
+    import numpy as np
+    import blockwise_scaled_fp8_amd as fp8
+    from synth import inputs
+    dev = torch.device("cuda", 0)
+    wq = torch.empty(groups, N, K, dtype=torch.uint8, device=dev)
+    wr = torch.empty(groups, cdiv(K, 128), cdiv(N, 128), dtype=torch.float32, device=dev).transpose(1, 2)
+    for g in range(groups):
+        w = inputs.linear_weight_bf16(N, K, seed=inputs.tensor_seed(seed + 100 + g, "w"), device=dev)
+        fp8.fp8_blockwise_quant(w, "128x128", q=wq[g], recip=wr[g])
+        del w
+    sizes = np.random.default_rng(seed).multinomial(M, np.ones(groups) / groups)
+    ends = torch.tensor(np.cumsum(sizes), dtype=torch.int32, device=dev)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    call = lambda: fp8.fp8_scaled_grouped_gemm_blockwise(wl.xq, wl.xr, wq, wr, ends, out=out)  # noqa: E731
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(stream)
+    for i in range(reps):
+        call()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(reps)) / reps
+    return {"groups": groups, "group_rows": [int(v) for v in sizes], "M": M, "N": N, "K": K,
+            "avg_us": round(ms * 1e3, 1), "tflops": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+
+
 def cpu_baseline(seed, min_seconds=10.0, max_samples=8):
     """The oracle, as it stands, on a bounded sample of the same workload.
     One sample: fwd and dgrad on 64 output rows (each with the full quantized
@@ -332,6 +367,7 @@ def main():
         "quant_us_per_step": round(rd["quant_us"], 1),
         "quant_gbps": round(rd["quant_gbps"], 1),
         "kernels": rd["kernels"]}
+    out["grouped_gemm"] = grouped_gemm(args.seed, r["workload"])
     del r, rd
     if not args.no_quant_standalone:
         out["quant_standalone"] = quant_standalone(args.seed)

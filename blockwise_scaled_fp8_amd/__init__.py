@@ -16,6 +16,7 @@ from .ops import (  # noqa: F401
     fp8_linear_wgrad,
     fp8_scaled_gemm_blockwise,
     fp8_scaled_gemm_tensorwise,
+    fp8_scaled_grouped_gemm_blockwise,
     fp8_tensorwise_quant,
     fp8bw_gemm_num_configs,
     linear_workspace,

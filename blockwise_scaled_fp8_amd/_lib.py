@@ -42,6 +42,9 @@ PROTOTYPES = {
                                                c_ptr, c_ptr, c_i64, c_int, c_ptr, c_size, c_ptr]),
     "fp8_scaled_gemm_tensorwise_bias": (c_int, [c_ptr, c_i64, c_ptr, c_ptr, c_i64, c_ptr, c_i64,
                                                 c_i64, c_i64, c_ptr, c_ptr, c_i64, c_int, c_ptr]),
+    "fp8_scaled_grouped_gemm_blockwise": (c_int, [c_ptr, c_i64, c_ptr, c_i64, c_ptr, c_i64, c_i64,
+                                                  c_ptr, c_i64, c_i64, c_i64, c_int, c_ptr, c_i64,
+                                                  c_i64, c_i64, c_ptr, c_i64, c_int, c_ptr]),
     "fp8bw_linear_ws_bytes": (c_size, [c_i64, c_i64, c_i64, c_int]),
     "fp8_linear_fwd": (c_int, [c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_size, c_ptr]),
     "fp8_linear_dgrad": (c_int, [c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_size, c_ptr]),

@@ -324,6 +324,45 @@ FP8BW_API int fp8_scaled_gemm_blockwise_bias(const void* a, int64_t lda, const f
                              M, N, K, out, ldo, out_dtype, -1, 0, ws, ws_bytes, stream, bias);
 }
 
+FP8BW_API int fp8_scaled_grouped_gemm_blockwise(
+    const void* a, int64_t lda, const float* ra, int64_t ra_s_kb, const void* b, int64_t ldb,
+    int64_t b_s_group, const float* rb, int64_t rb_s_row, int64_t rb_s_kb, int64_t rb_s_group,
+    int groups, const int* group_end, int64_t M, int64_t N, int64_t K, void* out, int64_t ldo,
+    int out_dtype, void* stream) {
+  if (groups < 1 || groups > (1 << 20)) return fail(FP8BW_ERR_SHAPE, "groups=%d must be in [1, 2^20]", groups);
+  int st = check_gemm_operands(a, lda, b, ldb, M, N, K, out, ldo, out_dtype);
+  if (st != FP8BW_OK) return st;
+  if (K % 128) return fail(FP8BW_ERR_SHAPE, "blockwise GEMM needs K %% 128 == 0 (K=%lld)", (long long)K);
+  if (M == 0 || N == 0) return ok();
+  if (!group_end) return fail(FP8BW_ERR_NULL, "group_end must be non-null");
+  if (!aligned(group_end, 4)) return fail(FP8BW_ERR_ALIGN, "group_end must be 4-byte aligned");
+  const int64_t kb = K / 128, nb = cdiv(N, 128);
+  if (b_s_group < (N - 1) * ldb + K || b_s_group % 16)
+    return fail(FP8BW_ERR_LAYOUT, "b_s_group=%lld must be >= (N-1)*ldb + K and a multiple of 16", (long long)b_s_group);
+  if (kb > 0) {
+    if (!ra || !rb) return fail(FP8BW_ERR_NULL, "ra and rb must be non-null");
+    if (!aligned(ra, 4) || !aligned(rb, 4)) return fail(FP8BW_ERR_ALIGN, "ra/rb must be 4-byte aligned");
+    if (kb > 1 && ra_s_kb < M) return fail(FP8BW_ERR_LAYOUT, "ra must be column-major: ra_s_kb >= M");
+    if (!strides_injective(nb, kb, rb_s_row, rb_s_kb))
+      return fail(FP8BW_ERR_LAYOUT, "rb strides (%lld, %lld) alias or are negative", (long long)rb_s_row, (long long)rb_s_kb);
+    const int64_t rb_extent = (nb - 1) * rb_s_row + (kb - 1) * rb_s_kb + 1;
+    if (groups > 1 && rb_s_group < rb_extent)
+      return fail(FP8BW_ERR_LAYOUT, "rb_s_group=%lld overlaps a group's %lld scales", (long long)rb_s_group, (long long)rb_extent);
+  }
+  fp8bw::GemmProblem p;
+  p.a = a; p.lda = lda; p.b = b; p.ldb = ldb;
+  p.ra = ra; p.ra_s_row = 1; p.ra_s_kb = ra_s_kb;
+  p.rb = rb; p.rb_s_row = rb_s_row; p.rb_s_kb = rb_s_kb;
+  p.out = out; p.ldo = ldo; p.M = M; p.N = N; p.K = K;
+  p.mode = fp8bw::kBlockB128;
+  p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
+  if (!fp8bw::grouped_gemm_ok(p, groups))
+    return fail(FP8BW_ERR_UNSUPPORTED, "grouped GEMM needs N >= 128 and 32-bit operand offsets");
+  return hip_status(fp8bw::launch_grouped_gemm(p, groups, group_end, b_s_group, rb_s_group,
+                                               (hipStream_t)stream),
+                    "fp8_scaled_grouped_gemm_blockwise");
+}
+
 static int gemm_tensorwise_impl(const void* a, int64_t lda, const float* ra, const void* b,
                                 int64_t ldb, const float* rb, int64_t M, int64_t N, int64_t K,
                                 void* out, int64_t ldo, int out_dtype, void* stream,

@@ -56,6 +56,13 @@ struct GemmArgs {
   // Optional bf16 bias [N], added to each output row after scaling and before
   // the output cast; nullptr for none.  Split-K adds it in the reduce.
   const uint16_t* bias;
+  // Grouped GEMM (large-tile kernel, no split): groups > 0 row groups of A
+  // and out, group g covering rows [group_end[g-1], group_end[g]) (device
+  // int32, cumulative, clamped to M), each with its own B (b + g*b_s_group)
+  // and B scales (rb + g*rb_s_group).
+  int groups;
+  const int* group_end;
+  int64_t b_s_group, rb_s_group;
 };
 
 __device__ __forceinline__ float bias_at(const uint16_t* bias, int n) {
@@ -391,8 +398,38 @@ __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM
   }
 }
 
+// Grouped GEMM: find the group and tile of (remapped) tile id t, and point
+// p at that group's rows of A, ra and out and at its B and B scales.  Tiles
+// are numbered group by group (tiles_m(g) x tiles_n each, grouped order
+// inside a group).  Returns false for ids past the last tile (the grid is
+// sized for the worst case of every group's last row tile being partial).
+template <int BM, int OUT>
+__device__ __forceinline__ bool locate_group_tile(GemmArgs& p, int t, int* tm, int* tn) {
+  int start = 0, row0 = 0;
+  for (int g = 0; g < p.groups; ++g) {
+    const int end = max(row0, min(p.group_end[g], p.M));
+    const int mg = end - row0;
+    const int mt = (mg + BM - 1) / BM;
+    const int nt = mt * p.tiles_n;
+    if (t < start + nt) {
+      tile_to_mn(t - start, mt, p.tiles_n, tm, tn);
+      p.a += (int64_t)row0 * p.lda;
+      p.ra += row0;
+      p.out = (uint8_t*)p.out + (int64_t)row0 * p.ldo * (OUT == kOutBf16 ? 2 : 4);
+      p.b += (int64_t)g * p.b_s_group;
+      p.rb += (int64_t)g * p.rb_s_group;
+      p.M = mg;
+      p.tiles_m = mt;
+      return true;
+    }
+    start += nt;
+    row0 = end;
+  }
+  return false;
+}
+
 template <int BM, int BN, int WGM, int WGN, int STAGES, int MODE, int OUT, bool SPLIT>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs p) {
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs p_in) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
@@ -432,8 +469,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const int wave = tid >> 6, lane = tid & 63;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   int tm, tn;
+  GemmArgs p = p_in;
   const int tile_local = xcd_remap(blockIdx.x, gridDim.x);
-  tile_to_mn(p.tile_base + tile_local, p.tiles_m, p.tiles_n, &tm, &tn);
+  if (p.groups > 0) {
+    if (!locate_group_tile<BM, OUT>(p, tile_local, &tm, &tn)) return;
+  } else {
+    tile_to_mn(p.tile_base + tile_local, p.tiles_m, p.tiles_n, &tm, &tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int kb_begin = blockIdx.y * p.kb_per_split;
   const int kb_end = min(p.kblocks, kb_begin + p.kb_per_split);
@@ -878,6 +920,9 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
   a.tile_base = 0;
   a.part_tiled = 0;
   a.bias = (const uint16_t*)p.bias;
+  a.groups = 0;
+  a.group_end = nullptr;
+  a.b_s_group = a.rb_s_group = 0;
   const int splits = pl.splits < 1 ? 1 : pl.splits;
   a.kb_per_split = a.kblocks == 0 ? 0 : (a.kblocks + splits - 1) / splits;
   hipError_t e;
@@ -914,6 +959,46 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
                        stream, (const float*)ws, splits, (int)p.M, (int)p.N, p.out, p.ldo,
                        (const uint16_t*)p.bias);
   return hipGetLastError();
+}
+
+// Grouped GEMM launch (see GemmArgs::groups).  The grid covers the worst
+// case, sum over groups of ceil(M_g / BM) <= ceil(M / BM) + groups row tiles,
+// times the column tiles; workgroups past the last tile return at once.
+bool grouped_gemm_ok(const GemmProblem& p, int groups) {
+  if (groups <= 0 || p.K % 128 || p.N < 128) return false;
+  return gemm_config_ok(p, p.N >= 256 ? 3 : 2);
+}
+
+hipError_t launch_grouped_gemm(const GemmProblem& p, int groups, const int* group_end,
+                               int64_t b_s_group, int64_t rb_s_group, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return hipSuccess;
+  const int cfg = p.N >= 256 ? 3 : 2;
+  const int bm = kCfgs[cfg].bm, bn = kCfgs[cfg].bn;
+  GemmArgs a = {};
+  a.a = (const uint8_t*)p.a;
+  a.b = (const uint8_t*)p.b;
+  a.ra = p.ra;
+  a.rb = p.rb;
+  a.out = p.out;
+  a.lda = p.lda;
+  a.ldb = p.ldb;
+  a.ldo = p.ldo;
+  a.ra_s_kb = p.ra_s_kb;
+  a.rb_s_row = p.rb_s_row;
+  a.rb_s_kb = p.rb_s_kb;
+  a.M = (int)p.M;
+  a.N = (int)p.N;
+  a.K = (int)p.K;
+  a.kblocks = (int)(p.K / 128);
+  a.kb_per_split = a.kblocks;
+  a.tiles_n = (int)((p.N + bn - 1) / bn);
+  a.tiles_m = 0;
+  a.groups = groups;
+  a.group_end = group_end;
+  a.b_s_group = b_s_group;
+  a.rb_s_group = rb_s_group;
+  const int64_t ntiles = ((p.M + bm - 1) / bm + groups) * a.tiles_n;
+  return launch_v2_cfg(cfg, a, p.mode, (int)ntiles, 1, p.out_kind, stream);
 }
 
 }  // namespace fp8bw

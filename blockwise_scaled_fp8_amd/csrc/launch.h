@@ -76,6 +76,11 @@ struct GemmPlan {
 GemmPlan gemm_plan(const GemmProblem& p, int config, int splits, bool allow_split);
 hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, void* ws, hipStream_t stream);
 // Fill a contiguous bf16 [rows, cols] matrix with +0.
+// Grouped blockwise GEMM: row groups of A / out ending at device int32
+// group_end[g] (cumulative), each with B + g*b_s_group and rb + g*rb_s_group.
+bool grouped_gemm_ok(const GemmProblem& p, int groups);
+hipError_t launch_grouped_gemm(const GemmProblem& p, int groups, const int* group_end,
+                               int64_t b_s_group, int64_t rb_s_group, hipStream_t stream);
 hipError_t launch_zero_bf16(void* out, int64_t rows, int64_t cols, hipStream_t stream);
 
 }  // namespace fp8bw

@@ -218,6 +218,36 @@ def fp8_scaled_gemm_tensorwise(a, ra, b, rb, out_dtype=torch.bfloat16, out=None,
     return out
 
 
+def fp8_scaled_grouped_gemm_blockwise(a, ra, b, rb, group_end, out_dtype=torch.bfloat16, out=None):
+    """Grouped blockwise GEMM: rows [group_end[g-1], group_end[g]) of a
+    (uint8 [M, K], ra fp32 [M, K/128] column-major) times b[g]^T (uint8
+    [G, N, K], rb fp32 [G, N/128, K/128], any strides) -> out [M, N].
+    group_end: device int32 [G], cumulative."""
+    lib = load_library()
+    _need_cuda(a, b, ra, rb, group_end)
+    _rowmajor(a, "a")
+    M, K = a.shape
+    if b.dim() != 3 or b.shape[2] != K or b.stride(2) != 1:
+        raise ValueError("b must be uint8 [G, N, K] with contiguous rows")
+    G, N = b.shape[0], b.shape[1]
+    if a.dtype != torch.uint8 or b.dtype != torch.uint8:
+        raise ValueError("codes are uint8 tensors")
+    kb = _cdiv(K, 128)
+    _check_shape(ra, (M, kb), "ra")
+    _check_shape(rb, (G, _cdiv(N, 128), kb), "rb")
+    if group_end.dtype != torch.int32 or group_end.shape != (G,) or group_end.stride(0) != 1:
+        raise ValueError("group_end must be a contiguous int32 [G] tensor")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check_shape(out, (M, N), "out")
+    check(lib.fp8_scaled_grouped_gemm_blockwise(
+        a.data_ptr(), a.stride(0), ra.data_ptr(), ra.stride(1), b.data_ptr(), b.stride(1),
+        b.stride(0), rb.data_ptr(), rb.stride(1), rb.stride(2), rb.stride(0), G,
+        group_end.data_ptr(), M, N, K, out.data_ptr(), out.stride(0), OUT_DTYPES[out.dtype],
+        _stream(a)))
+    return out
+
+
 def linear_workspace(M, N, K, which, device):
     n = load_library().fp8bw_linear_ws_bytes(M, N, K, which)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

@@ -216,6 +216,38 @@ int fp8_scaled_gemm_tensorwise(const void* a, int64_t lda, const float* ra, cons
  *   Every other argument, status and workspace rule is that of the call
  *   without _bias.
  */
+/*
+ * fp8_scaled_grouped_gemm_blockwise -- one launch for G GEMMs that share N
+ * and K and split the rows of A and out into consecutive groups, each with
+ * its own B (the mixture-of-experts layout: tokens sorted by expert, one
+ * weight per expert; the pages mention the grouped scaled matmul of MoE
+ * training in [INTEG]'s review discussion).  For every group g and row m of
+ * it, out[m, :] is what fp8_scaled_gemm_blockwise gives for that row with B_g
+ * (1x128 A scales, 128x128 B scales):
+ *
+ *   rows of group g: [group_end[g-1], group_end[g])   (group_end[-1] = 0)
+ *   B_g  = b  + g * b_s_group   [N, K] codes, leading dim ldb
+ *   rb_g = rb + g * rb_s_group  scales of B_g, rb_g[(n/128)*rb_s_row + kb*rb_s_kb]
+ *
+ *   a, ra       device [M, K] codes and their column-major 1x128 scales
+ *               ra[m + kb*ra_s_kb] (ra_s_kb >= M) for all groups' rows.
+ *   group_end   DEVICE int32 [groups], cumulative row ends, read by the
+ *               kernel (no host synchronization).  Values are clamped to
+ *               [previous end, M]: a malformed table cannot make the kernel
+ *               read or write outside A, ra and out.  Rows past the last end
+ *               are not written.
+ *   b_s_group   >= (N-1)*ldb + K, a multiple of 16 (distinct weights).
+ *   rb_s_group  large enough that groups' scale grids do not overlap.
+ *   Requires K % 128 == 0, N >= 128 and 32-bit byte offsets within A and
+ *   within each B_g (else FP8BW_ERR_UNSUPPORTED); no split-K, no workspace.
+ */
+int fp8_scaled_grouped_gemm_blockwise(const void* a, int64_t lda, const float* ra,
+                                      int64_t ra_s_kb, const void* b, int64_t ldb,
+                                      int64_t b_s_group, const float* rb, int64_t rb_s_row,
+                                      int64_t rb_s_kb, int64_t rb_s_group, int groups,
+                                      const int* group_end, int64_t M, int64_t N, int64_t K,
+                                      void* out, int64_t ldo, int out_dtype, void* stream);
+
 int fp8_scaled_gemm_blockwise_bias(const void* a, int64_t lda, const float* ra, int64_t ra_s_row,
                                    int64_t ra_s_kb, const void* b, int64_t ldb, const float* rb,
                                    int64_t rb_s_row, int64_t rb_s_kb, int b_block, int64_t M,

@@ -120,6 +120,27 @@ def tensorwise_bound(a_codes, ra, b_codes, rb):
     return (A @ B.T) * abs(float(np.float32(ra)) * float(np.float32(rb)))
 
 
+def grouped_blockwise_gemm(a_codes, ra, b_codes, rb, group_end, with_bound=False):
+    """Grouped blockwise GEMM (mixture-of-experts layout): rows
+    [group_end[g-1], group_end[g]) of A are multiplied by B_g^T with B_g's
+    128x128 scales rb[g]; rows past the last end are NaN (not written).
+    Each group is exactly blockwise_gemm on its rows.  Returns ref64 [M, N]
+    (and S with with_bound)."""
+    a_codes = np.asarray(a_codes)
+    M, N = a_codes.shape[0], b_codes.shape[1]
+    ref = np.full((M, N), np.nan)
+    S = np.full((M, N), np.nan)
+    start = 0
+    for g, end in enumerate(np.asarray(group_end, dtype=np.int64)):
+        end = min(max(int(end), start), M)
+        if end > start:
+            r, s = blockwise_gemm(a_codes[start:end], np.asarray(ra)[start:end], b_codes[g],
+                                  rb[g], "128x128", with_bound=True)
+            ref[start:end], S[start:end] = r, s
+        start = end
+    return (ref, S) if with_bound else ref
+
+
 def add_bias(ref, bias_bits):
     """Bias epilogue: out[m, n] = ref[m, n] + bias[n], the bf16 bias widened
     exactly, in float64.  Both GEMM interfaces on the pages take an optional

@@ -151,6 +151,28 @@ def test_bias_entry_points_validate(lib):
                                                0, None) == SHAPE   # K % 16
 
 
+def _grouped(lib, **kw):
+    a = dict(a=P, lda=256, ra=P, ra_s_kb=64, b=P, ldb=256, b_s_group=128 * 256, rb=P, rb_s_row=1,
+             rb_s_kb=1, rb_s_group=2, groups=4, group_end=P, M=64, N=128, K=256, out=P, ldo=128,
+             out_dtype=0, stream=None)
+    a.update(kw)
+    return lib.fp8_scaled_grouped_gemm_blockwise(*[a[k] for k in (
+        "a", "lda", "ra", "ra_s_kb", "b", "ldb", "b_s_group", "rb", "rb_s_row", "rb_s_kb",
+        "rb_s_group", "groups", "group_end", "M", "N", "K", "out", "ldo", "out_dtype", "stream")])
+
+
+def test_grouped_gemm_validation(lib):
+    assert _grouped(lib, groups=0) == SHAPE
+    assert _grouped(lib, K=200) == SHAPE
+    assert _grouped(lib, group_end=None) == NULL
+    assert _grouped(lib, group_end=P + 2) == ALIGN
+    assert _grouped(lib, b_s_group=100) == LAYOUT           # groups' weights overlap
+    assert _grouped(lib, ra_s_kb=8) == LAYOUT               # ra not column-major
+    assert _grouped(lib, rb_s_group=1) == LAYOUT            # groups' scales overlap
+    assert _grouped(lib, N=64, ldo=64) == UNSUP             # N < 128
+    assert _grouped(lib, M=0, a=None, out=None, group_end=None) == OK
+
+
 def test_tensorwise_validation(lib):
     f = lib.fp8_scaled_gemm_tensorwise
     assert f(P, 32, P, P, 32, P, 16, 32, 24, P, 32, 1, None) == SHAPE        # K % 16

@@ -1,0 +1,85 @@
+"""GPU parity of the grouped (mixture-of-experts) blockwise GEMM against the
+oracle: each row uses its group's weight; empty groups, groups smaller than
+a tile, rows past the last boundary (left untouched) and a malformed
+boundary table (clamped, no access outside the operands)."""
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_scaled_fp8_amd as fp8
+from oracle import gemm
+from tests.gpu_util import check_gemm_output, host_f32, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E
+    return c
+
+
+def _case(gpu, G, M, N, K, ends, od, seed, sample=None):
+    rng = np.random.default_rng(seed)
+    a = _codes(rng, (M, K))
+    b = np.stack([_codes(rng, (N, K)) for _ in range(G)])
+    ra = rng.uniform(1e-3, 2e-3, (M, K // 128)).astype(np.float32)
+    rb = rng.uniform(1e-3, 2e-3, (G, -(-N // 128), K // 128)).astype(np.float32)
+    dt = torch.bfloat16 if od == "bf16" else torch.float32
+    out = torch.full((M, N), float("nan"), dtype=dt, device=gpu)
+    ra_d = torch.from_numpy(np.ascontiguousarray(ra.T)).to(gpu).t()
+    # per-group column-major scale grids, groups side by side
+    rb_d = torch.from_numpy(np.ascontiguousarray(rb.transpose(0, 2, 1))).to(gpu).transpose(1, 2)
+    say("grouped gemm", G, M, N, K, od, list(ends)[:8])
+    fp8.fp8_scaled_grouped_gemm_blockwise(
+        torch.from_numpy(a).to(gpu), ra_d, torch.from_numpy(b).to(gpu), rb_d,
+        torch.tensor(ends, dtype=torch.int32, device=gpu), out=out)
+    torch.cuda.synchronize()
+    got = host_f32(out)
+    rows = np.arange(M) if sample is None else sample
+    bounds = np.minimum(np.maximum.accumulate(np.clip(np.asarray(ends, np.int64), 0, M)), M)
+    refs, bnds, keep = [], [], []
+    for m in rows:
+        g = int(np.searchsorted(bounds, m, side="right"))
+        if g >= G:
+            assert np.all(np.isnan(got[m])), f"row {m} past the last group was written"
+            continue
+        ref, S = gemm.blockwise_gemm(a[[m]], ra[[m]], b[g], rb[g], "128x128", with_bound=True)
+        refs.append(ref)
+        bnds.append(S)
+        keep.append(m)
+    # one check over all written rows (the Frobenius bar is a whole-output bar)
+    check_gemm_output(got[keep], np.concatenate(refs), np.concatenate(bnds), K // 128, od,
+                      f"grouped {G}x{M}x{N}x{K}")
+    return got
+
+
+def test_grouped_ragged_groups_and_unwritten_tail(gpu):
+    _case(gpu, 4, 1024, 512, 1024, [300, 300, 700, 1000], "bf16", seed=50)
+
+
+def test_grouped_single_group_equals_plain_gemm(gpu):
+    rng = np.random.default_rng(51)
+    M, N, K = 640, 384, 512
+    got = _case(gpu, 1, M, N, K, [M], "f32", seed=51, sample=np.r_[0, 1, 255, 256, 639])
+    assert np.isfinite(got).all()
+    del rng
+
+
+def test_grouped_narrow_n_uses_the_256x128_tiles(gpu):
+    _case(gpu, 3, 520, 128, 768, [17, 260, 520], "f32", seed=52)
+
+
+def test_grouped_moe_like_sampled(gpu):
+    rng = np.random.default_rng(53)
+    G, M, N, K = 16, 8192, 2048, 2048
+    sizes = rng.multinomial(M, np.ones(G) / G)
+    ends = np.cumsum(sizes)
+    sample = np.unique(np.r_[ends[:-1] - 1, ends[:-1], 0, M - 1, rng.integers(0, M, 24)])
+    _case(gpu, G, M, N, K, ends, "bf16", seed=53, sample=sample)
+
+
+def test_grouped_malformed_table_is_clamped(gpu):
+    """Decreasing ends and ends past M are clamped to [previous end, M]."""
+    _case(gpu, 4, 512, 256, 256, [200, 100, 9999, 50], "f32", seed=54)

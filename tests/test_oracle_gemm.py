@@ -238,3 +238,27 @@ def test_bias_epilogue_against_fraction_and_invariants():
     assert np.array_equal(gemm.add_bias(ref, np.zeros(N, np.uint16)), ref)
     with pytest.raises(ValueError):
         gemm.add_bias(ref, bias[:M])
+
+
+def test_grouped_gemm_rows_use_their_groups_weights():
+    """Each output row equals the dequantized row times the dequantized
+    weight of the group that contains it (group membership computed here
+    from the boundaries, per row, with a plain float64 product): a wrong
+    boundary, an off-by-one or a swapped weight fails.  Empty groups and
+    rows past the last boundary (left unwritten) included."""
+    rng = np.random.default_rng(11)
+    G, M, N, K = 4, 40, 130, 256
+    a = _random_codes(rng, (M, K))
+    b = np.stack([_random_codes(rng, (N, K)) for _ in range(G)])
+    ra = rng.uniform(0.5, 2, (M, 2)).astype(np.float32)
+    rb = rng.uniform(0.5, 2, (G, 2, 2)).astype(np.float32)
+    ends = np.array([7, 7, 30, 37], np.int32)          # group 1 empty; rows 37.. unwritten
+    ref = gemm.grouped_blockwise_gemm(a, ra, b, rb, ends)
+    A = e4m3.decode(a) * np.repeat(ra.astype(np.float64), 128, axis=1)
+    for m in range(M):
+        g = int(np.searchsorted(ends, m, side="right"))
+        if g >= G:
+            assert np.all(np.isnan(ref[m]))
+            continue
+        Bg = e4m3.decode(b[g]) * np.repeat(np.repeat(rb[g].astype(np.float64), 128, axis=0)[:N], 128, axis=1)
+        np.testing.assert_allclose(ref[m], A[m] @ Bg.T, rtol=1e-12, atol=1e-9)
