@@ -98,6 +98,8 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int half)
 
 // How many 16-row A sub-tiles ahead the large-tile kernel reads fragments.
 constexpr int kRowPrefetch = 1;
+// MFMA steps between a partial's MFMA and its rescale (ring of delay + 1).
+constexpr int kRingDelay = 2;
 
 // Fragment read at precomputed byte offsets of its two 16-byte chunks.
 __device__ __forceinline__ v8i load_frag_at(const uint8_t* tile, uint32_t lo, uint32_t hi) {
@@ -332,18 +334,21 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 // One stage of direct global->LDS loads for K block kb (see gemm_v2_kernel).
 template <int AI, int BI, int RAI, int RBI, int RAB, int RBB, int NW, int MODE>
 __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* sa, uint8_t* sb,
-                                            float* sra, float* srb, const uint32_t (&aoff)[AI],
-                                            const uint32_t (&boff)[BI], int wave, int lane,
-                                            int m0, int n0) {
+                                            float* sra, float* srb, int arow, int brow,
+                                            uint32_t chunk16, int wave, int lane, int m0, int n0) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel stub
   const uint8_t* ga = p.a + (int64_t)kb * 128;
   const uint8_t* gb = p.b + (int64_t)kb * 128;
 #pragma unroll
   for (int i = 0; i < AI; ++i)
-    __builtin_amdgcn_global_load_lds(ga + aoff[i], (lds_void_t*)(sa + (wave + NW * i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        ga + (uint32_t)(min(arow + 8 * NW * i, p.M - 1) * (uint32_t)p.lda + chunk16),
+        (lds_void_t*)(sa + (wave + NW * i) * 1024), 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < BI; ++i)
-    __builtin_amdgcn_global_load_lds(gb + boff[i], (lds_void_t*)(sb + (wave + NW * i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        gb + (uint32_t)(min(brow + 8 * NW * i, p.N - 1) * (uint32_t)p.ldb + chunk16),
+        (lds_void_t*)(sb + (wave + NW * i) * 1024), 16, 0, 0);
   if constexpr (MODE != kTensorwise) {
 #pragma unroll
     for (int i = 0; i < RAI; ++i) {
@@ -488,21 +493,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   static_assert(NW % 2 == 0, "octet parity must be the wave parity");
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ ((4 * (wave & 1) + (lrow >> 1)) & 7);
-  uint32_t aoff[AI], boff[BI];
-#pragma unroll
-  for (int i = 0; i < AI; ++i) {
-    const int r = min(m0 + 8 * (wave + NW * i) + lrow, p.M - 1);
-    aoff[i] = (uint32_t)((int64_t)r * p.lda) + lchunk * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < BI; ++i) {
-    const int r = min(n0 + 8 * (wave + NW * i) + lrow, p.N - 1);
-    boff[i] = (uint32_t)((int64_t)r * p.ldb) + lchunk * 16;
-  }
+  // Row of this lane in its wave's first A / B row octet; octet i of the
+  // wave is 8 NW rows further (clamped to the last row at ragged edges).
+  // The per-load offsets are recomputed each K block from these (made opaque
+  // there) rather than held in registers.
+  int arow = m0 + 8 * wave + lrow, brow = n0 + 8 * wave + lrow;
+  uint32_t chunk16 = lchunk * 16;
 
 #define FP8BW_ISSUE(kb, st)                                                                  \
   issue_stage<AI, BI, RAI, RBI, RAB, RBB, NW, MODE>(p, (kb), sA[st], sB[st], sRa[st], sRb[st], \
-                                                    aoff, boff, wave, lane, m0, n0)
+                                                    arow, brow, chunk16, wave, lane, m0, n0)
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -546,7 +546,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     uint32_t b_hi = (wn0 + frow) * 128 + (((2 * fhalf + 1) ^ swz(wn0 + frow)) << 4);
     uint32_t ra_off = (wm0 + 4 * fhalf) * 4;
     uint32_t rb_off = (wn0 + frow) * 4;
-    asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(ra_off), "+v"(rb_off));
+    asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(ra_off), "+v"(rb_off),
+                 "+v"(arow), "+v"(brow), "+v"(chunk16));
     const uint8_t* tA = sA[st];
     const uint8_t* tB = sB[st];
     const uint8_t* tRa = (const uint8_t*)sRa[st];
@@ -583,9 +584,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
         if constexpr (MODE == kBlockB128) sa[i] = sa[i] * sbn;
       }
     }
-    v4f ring[3];
+    v4f ring[kRingDelay + 1];
 #pragma unroll
-    for (int t = 0; t < T + 2; ++t) {
+    for (int t = 0; t < T + kRingDelay; ++t) {
       const int i = t / TN, j = t % TN;
       if (t < T && j == 0 && i + PF < TM)
         af[(i + PF) % NS] = load_frag_at(tA, a_lo + 2048 * (i + PF), a_hi + 2048 * (i + PF));
@@ -593,17 +594,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
         if (MODE == kTensorwise)
           acc[i][j] = mfma_fp8(af[i % NS], bf[j], acc[i][j]);
         else
-          ring[t % 3] = mfma_fp8(af[i % NS], bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+          ring[t % (kRingDelay + 1)] = mfma_fp8(af[i % NS], bf[j], v4f{0.f, 0.f, 0.f, 0.f});
       }
       if constexpr (SCALED) {
-        if (t >= 2) {
-          const int u = t - 2, iu = u / TN, ju = u % TN;
+        if (t >= kRingDelay) {
+          const int u = t - kRingDelay, iu = u / TN, ju = u % TN;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             if constexpr (MODE == kBlockB128)
-              acc[iu][ju][v] = __builtin_fmaf(ring[u % 3][v], sa[iu % NS][v], acc[iu][ju][v]);
+              acc[iu][ju][v] = __builtin_fmaf(ring[u % (kRingDelay + 1)][v], sa[iu % NS][v], acc[iu][ju][v]);
             else
-              acc[iu][ju][v] = __builtin_fmaf(ring[u % 3][v] * sbc[ju], sa[iu % NS][v], acc[iu][ju][v]);
+              acc[iu][ju][v] = __builtin_fmaf(ring[u % (kRingDelay + 1)][v] * sbc[ju], sa[iu % NS][v], acc[iu][ju][v]);
           }
         }
         if (t < T && j == 1 && i + PF < TM) {
