@@ -314,6 +314,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quant-standalone", action="store_true",
                     help="skip the standalone 32768^2 quantizer timing")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step alone: no fused-quantization step, grouped GEMM or "
+                         "standalone quantizers (for profiling runs)")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -359,15 +362,19 @@ def main():
         "kernels": r["kernels"],
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
     }
-    rd = run_gpu(args.steps, args.warmup, args.seed, plan_fn=step_plan_dual, wl=r["workload"])
-    out["fused_quant_step"] = {
-        "note": "same step, each bf16 tensor quantized once into both layouts",
-        "ms_per_step": round(rd["gpu_ms_per_step"], 4),
-        "value": round(flops / (rd["gpu_ms_per_step"] * 1e-3) / 1e12, 1),
-        "quant_us_per_step": round(rd["quant_us"], 1),
-        "quant_gbps": round(rd["quant_gbps"], 1),
-        "kernels": rd["kernels"]}
-    out["grouped_gemm"] = grouped_gemm(args.seed, r["workload"])
+    if args.step_only:
+        args.no_quant_standalone = True
+    rd = (None if args.step_only else
+          run_gpu(args.steps, args.warmup, args.seed, plan_fn=step_plan_dual, wl=r["workload"]))
+    if rd is not None:
+        out["fused_quant_step"] = {
+            "note": "same step, each bf16 tensor quantized once into both layouts",
+            "ms_per_step": round(rd["gpu_ms_per_step"], 4),
+            "value": round(flops / (rd["gpu_ms_per_step"] * 1e-3) / 1e12, 1),
+            "quant_us_per_step": round(rd["quant_us"], 1),
+            "quant_gbps": round(rd["quant_gbps"], 1),
+            "kernels": rd["kernels"]}
+        out["grouped_gemm"] = grouped_gemm(args.seed, r["workload"])
     del r, rd
     if not args.no_quant_standalone:
         out["quant_standalone"] = quant_standalone(args.seed)
