@@ -278,14 +278,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
 
 // ---------------------------------------------------------------------------
 // Large-tile kernel: BM x BN workgroup tile, WGM x WGN waves, STAGES-deep
-// LDS ring filled by direct global->LDS loads (global_load_lds_dwordx4: each
-// lane's 16 bytes land at LDS base + 16 * lane, so a wave instruction fills
-// one 1 KB "row octet" = 8 rows x 128 bytes; the XOR swizzle is applied by
-// choosing which global chunk each lane fetches).  Scales ride the same ring
-// via 4-byte direct loads.  The compiler does not order these LDS writes
-// against later LDS reads, so the kernel waits with explicit vmcnt counts:
-// every wave issues exactly LPS loads per stage, and before consuming stage
-// kb+1 it waits until at most the loads of later stages are outstanding.
+// LDS ring filled by direct buffer->LDS loads (buffer_load_dwordx4 ... lds:
+// each lane's 16 bytes land at LDS base + 16 * lane, so a wave instruction
+// fills one 1 KB "row octet" = 8 rows x 128 bytes; the XOR swizzle is
+// applied by choosing which global chunk each lane fetches).  Scales ride
+// the same ring via 4-byte direct loads.  The buffer (MUBUF) form is used
+// rather than the global (FLAT) one because the compiler's wait insertion
+// treats an outstanding FLAT load into LDS as possibly pending on the LDS
+// counter too and then waits for every LDS read to return (lgkmcnt(0))
+// before using any; with MUBUF loads the fragment reads get exact counts.
+// The compiler does not order these LDS writes against later LDS reads, so
+// the kernel waits with explicit vmcnt counts: every wave issues exactly
+// LPS loads per stage, and before consuming stage kb+1 it waits until at
+// most the loads of later stages are outstanding.
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -331,43 +336,58 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   return x * full + min(x, rem) + q;
 }
 
-// One stage of direct global->LDS loads for K block kb (see gemm_v2_kernel).
+// Raw buffer descriptor over `bytes` bytes from `base` (stride 0; gfx9
+// dword3: 32-bit data format, no swizzle).  The hardware range check makes
+// any access at or past `bytes` read as zero, which is how ragged row tiles
+// get their missing rows.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+// One stage of direct buffer->LDS loads for K block kb (see gemm_v2_kernel).
+// ars / brs cover the tile's rows of A / B from its first row on; a_voff /
+// b_voff are this lane's byte offsets in its wave's first row octet, and
+// octet i is 8 NW rows further (soffset), K block kb 128 bytes further.
 template <int AI, int BI, int RAI, int RBI, int RAB, int RBB, int NW, int MODE>
 __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* sa, uint8_t* sb,
-                                            float* sra, float* srb, int arow, int brow,
-                                            uint32_t chunk16, int wave, int lane, int m0, int n0) {
+                                            float* sra, float* srb, __amdgpu_buffer_rsrc_t ars,
+                                            __amdgpu_buffer_rsrc_t brs, uint32_t a_voff,
+                                            uint32_t b_voff, uint32_t rbn_voff, int wave, int lane,
+                                            int m0, int n0) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel stub
-  const uint8_t* ga = p.a + (int64_t)kb * 128;
-  const uint8_t* gb = p.b + (int64_t)kb * 128;
+  const int ko = kb * 128;
 #pragma unroll
   for (int i = 0; i < AI; ++i)
-    __builtin_amdgcn_global_load_lds(
-        ga + (uint32_t)(min(arow + 8 * NW * i, p.M - 1) * (uint32_t)p.lda + chunk16),
-        (lds_void_t*)(sa + (wave + NW * i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void_t*)(sa + (wave + NW * i) * 1024), 16,
+                                             a_voff, ko + 8 * NW * i * (int)p.lda, 0, 0);
 #pragma unroll
   for (int i = 0; i < BI; ++i)
-    __builtin_amdgcn_global_load_lds(
-        gb + (uint32_t)(min(brow + 8 * NW * i, p.N - 1) * (uint32_t)p.ldb + chunk16),
-        (lds_void_t*)(sb + (wave + NW * i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void_t*)(sb + (wave + NW * i) * 1024), 16,
+                                             b_voff, ko + 8 * NW * i * (int)p.ldb, 0, 0);
   if constexpr (MODE != kTensorwise) {
+    const __amdgpu_buffer_rsrc_t rars =
+        buffer_rsrc(p.ra + (int64_t)kb * p.ra_s_kb + m0, (int64_t)(p.M - m0) * 4);
 #pragma unroll
     for (int i = 0; i < RAI; ++i) {
       const int blk = (wave + NW * i) % RAB;
-      const int r = min(m0 + 64 * blk + lane, p.M - 1);
-      __builtin_amdgcn_global_load_lds(p.ra + (int64_t)kb * p.ra_s_kb + r,
-                                       (lds_void_t*)(sra + 64 * blk), 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rars, (lds_void_t*)(sra + 64 * blk), 4, lane * 4,
+                                               256 * blk, 0, 0);
     }
+    if constexpr (MODE == kBlockB128) {
+      const __amdgpu_buffer_rsrc_t rbrs = buffer_rsrc(
+          p.rb + (int64_t)kb * p.rb_s_kb, ((int64_t)((p.N - 1) / 128) * p.rb_s_row + 1) * 4);
 #pragma unroll
-    for (int i = 0; i < RBI; ++i) {
-      if constexpr (MODE == kBlockB128) {
-        const int nb = min(n0 / 128 + lane, (p.N - 1) / 128);
-        __builtin_amdgcn_global_load_lds(p.rb + (int64_t)nb * p.rb_s_row + (int64_t)kb * p.rb_s_kb,
-                                         (lds_void_t*)srb, 4, 0, 0);
-      } else {
+      for (int i = 0; i < RBI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbrs, (lds_void_t*)srb, 4, rbn_voff, 0, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t rbrs =
+          buffer_rsrc(p.rb + (int64_t)kb * p.rb_s_kb + n0, (int64_t)(p.N - n0) * 4);
+#pragma unroll
+      for (int i = 0; i < RBI; ++i) {
         const int blk = (wave + NW * i) % RBB;
-        const int c = min(n0 + 64 * blk + lane, p.N - 1);
-        __builtin_amdgcn_global_load_lds(p.rb + (int64_t)kb * p.rb_s_kb + c,
-                                         (lds_void_t*)(srb + 64 * blk), 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbrs, (lds_void_t*)(srb + 64 * blk), 4, lane * 4,
+                                                 256 * blk, 0, 0);
       }
     }
   }
@@ -471,7 +491,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   float* const sRb[3] = {sRb0, sRb1, sRb2};
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   int tm, tn;
   GemmArgs p = p_in;
@@ -485,24 +505,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const int kb_begin = blockIdx.y * p.kb_per_split;
   const int kb_end = min(p.kblocks, kb_begin + p.kb_per_split);
 
-  // Per-lane global byte offsets of this wave's row octets (k offset added
-  // per stage).  Lane 8q + c of a DMA instruction fills physical chunk c of
-  // row 8o + q (o = octet index), which holds logical chunk c ^ swz(8o + q);
-  // swz(8o + q) = (4 (o & 1) + (q >> 1)) & 7 and o & 1 == wave & 1 because
-  // the octets of a wave step by NW (even).
+  // Per-lane byte offsets of this wave's first row octets of A and B.  Lane
+  // 8q + c of a direct-load instruction fills physical chunk c of row 8o + q
+  // (o = octet index), which holds logical chunk c ^ swz(8o + q); swz(8o + q)
+  // = (4 (o & 1) + (q >> 1)) & 7 and o & 1 == wave & 1 because the octets of
+  // a wave step by NW (even).
   static_assert(NW % 2 == 0, "octet parity must be the wave parity");
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ ((4 * (wave & 1) + (lrow >> 1)) & 7);
-  // Row of this lane in its wave's first A / B row octet; octet i of the
-  // wave is 8 NW rows further (clamped to the last row at ragged edges).
-  // The per-load offsets are recomputed each K block from these (made opaque
-  // there) rather than held in registers.
-  int arow = m0 + 8 * wave + lrow, brow = n0 + 8 * wave + lrow;
-  uint32_t chunk16 = lchunk * 16;
+  const uint32_t a_voff = (uint32_t)((8 * wave + lrow) * p.lda + lchunk * 16);
+  const uint32_t b_voff = (uint32_t)((8 * wave + lrow) * p.ldb + lchunk * 16);
+  const __amdgpu_buffer_rsrc_t ars =
+      buffer_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)(p.M - m0) * p.lda);
+  const __amdgpu_buffer_rsrc_t brs =
+      buffer_rsrc(p.b + (int64_t)n0 * p.ldb, (int64_t)(p.N - n0) * p.ldb);
+  // 128x128 B scales: lane l loads the scale of column block n0 / 128 + l
+  // (clamped to the last block).
+  const uint32_t rbn_voff = (uint32_t)(min(n0 / 128 + lane, (p.N - 1) / 128) * p.rb_s_row * 4);
 
 #define FP8BW_ISSUE(kb, st)                                                                  \
   issue_stage<AI, BI, RAI, RBI, RAB, RBB, NW, MODE>(p, (kb), sA[st], sB[st], sRa[st], sRb[st], \
-                                                    arow, brow, chunk16, wave, lane, m0, n0)
+                                                    ars, brs, a_voff, b_voff, rbn_voff, wave, \
+                                                    lane, m0, n0)
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -546,8 +570,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     uint32_t b_hi = (wn0 + frow) * 128 + (((2 * fhalf + 1) ^ swz(wn0 + frow)) << 4);
     uint32_t ra_off = (wm0 + 4 * fhalf) * 4;
     uint32_t rb_off = (wn0 + frow) * 4;
-    asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(ra_off), "+v"(rb_off),
-                 "+v"(arow), "+v"(brow), "+v"(chunk16));
+    asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(ra_off), "+v"(rb_off));
     const uint8_t* tA = sA[st];
     const uint8_t* tB = sB[st];
     const uint8_t* tRa = (const uint8_t*)sRa[st];
@@ -740,11 +763,12 @@ bool gemm_config_ok(const GemmProblem& p, int cfg) {
   if (cfg < 0 || cfg >= kNumCfgs) return false;
   if (kCfgs[cfg].kind == 1) {
     // The large-tile kernels load whole 128-byte K blocks (no K tail) and
-    // address operands with 32-bit byte offsets.
+    // address a row tile of A or B (at most 256 rows) and a column of B
+    // block scales with signed 32-bit buffer offsets.
     if (p.K % 128) return false;
-    if ((p.M - 1) * p.lda + p.K >= ((int64_t)1 << 32) ||
-        (p.N - 1) * p.ldb + p.K >= ((int64_t)1 << 32))
-      return false;
+    const int64_t lim = (int64_t)1 << 31;
+    if (256 * p.lda + p.K >= lim || 256 * p.ldb + p.K >= lim) return false;
+    if (((p.N + 127) / 128) * p.rb_s_row * 4 >= lim) return false;
   }
   return true;
 }

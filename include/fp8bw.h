@@ -238,8 +238,9 @@ int fp8_scaled_gemm_tensorwise(const void* a, int64_t lda, const float* ra, cons
  *               are not written.
  *   b_s_group   >= (N-1)*ldb + K, a multiple of 16 (distinct weights).
  *   rb_s_group  large enough that groups' scale grids do not overlap.
- *   Requires K % 128 == 0, N >= 128 and 32-bit byte offsets within A and
- *   within each B_g (else FP8BW_ERR_UNSUPPORTED); no split-K, no workspace.
+ *   Requires K % 128 == 0, N >= 128 and 256*lda + K, 256*ldb + K < 2^31
+ *   (a 256-row tile is addressed with signed 32-bit byte offsets; else
+ *   FP8BW_ERR_UNSUPPORTED); no split-K, no workspace.
  */
 int fp8_scaled_grouped_gemm_blockwise(const void* a, int64_t lda, const float* ra,
                                       int64_t ra_s_kb, const void* b, int64_t ldb,
