@@ -354,7 +354,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // ars / brs cover the tile's rows of A / B from its first row on; a_voff /
 // b_voff are this lane's byte offsets in its wave's first row octet, and
 // octet i is 8 NW rows further (soffset), K block kb 128 bytes further.
-template <int AI, int BI, int RAI, int RBI, int RAB, int RBB, int NW, int MODE>
+template <int AI, int BI, int RAI, int RBI, int RAB, int RBB, int NW, int MODE, int TMV>
 __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* sa, uint8_t* sb,
                                             float* sra, float* srb, __amdgpu_buffer_rsrc_t ars,
                                             __amdgpu_buffer_rsrc_t brs, uint32_t a_voff,
@@ -373,11 +373,16 @@ __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* 
   if constexpr (MODE != kTensorwise) {
     const __amdgpu_buffer_rsrc_t rars =
         buffer_rsrc(p.ra + (int64_t)kb * p.ra_s_kb + m0, (int64_t)(p.M - m0) * 4);
+    // ra lands transposed per wave row band of 16 TMV rows: LDS slot
+    // k = 16 TMV h + TMV r + i holds row 16 TMV h + 16 i + r, so that a lane
+    // (fragment row r) finds the scales of its TMV sub-tiles side by side.
 #pragma unroll
     for (int i = 0; i < RAI; ++i) {
       const int blk = (wave + NW * i) % RAB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rars, (lds_void_t*)(sra + 64 * blk), 4, lane * 4,
-                                               256 * blk, 0, 0);
+      const int k = 64 * blk + lane;
+      const int row = (k / (16 * TMV)) * (16 * TMV) + 16 * (k % TMV) + (k % (16 * TMV)) / TMV;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rars, (lds_void_t*)(sra + 64 * blk), 4, row * 4,
+                                               0, 0, 0);
     }
     if constexpr (MODE == kBlockB128) {
       const __amdgpu_buffer_rsrc_t rbrs = buffer_rsrc(
@@ -399,28 +404,56 @@ __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* 
 #endif
 }
 
+// Epilogue of the large-tile kernels: lane (frow, fhalf) holds, for each
+// sub-tile (i, j), row mb + 16 i + frow and the four columns
+// nb + 16 j + 4 fhalf + v.  The four are stored with one 8-byte (bf16) or
+// 16-byte (fp32) store when the output rows allow it, else one by one.
 template <bool GUARD, int TM, int TN, int MODE, int OUT, bool SPLIT>
 __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM][TN], float tscale,
                                           int mb, int nb, int frow, int fhalf, float* pbase,
                                           int64_t pld, int pm0, int pn0) {
+  const bool vec = SPLIT ? ((pld & 3) == 0 && ((size_t)pbase & 15) == 0)
+                         : ((p.ldo & 3) == 0 && ((size_t)p.out & 15) == 0);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int m = mb + 16 * i + frow;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = nb + 16 * j + frow;
+      const int nq = nb + 16 * j + 4 * fhalf;
+      float val[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = mb + 16 * i + 4 * fhalf + v;
-        if (!GUARD || (m < p.M && n < p.N)) {
-          float val = acc[i][j][v];
-          if constexpr (MODE == kTensorwise) val *= tscale;
-          if constexpr (!SPLIT) val += bias_at(p.bias, n);
-          if constexpr (SPLIT) {
-            pbase[(int64_t)(m - pm0) * pld + (n - pn0)] = val;
-          } else if constexpr (OUT == kOutBf16) {
-            ((uint16_t*)p.out)[(int64_t)m * p.ldo + n] = (uint16_t)f32_to_bf16_rne(val);
-          } else {
-            ((float*)p.out)[(int64_t)m * p.ldo + n] = val;
+        val[v] = acc[i][j][v];
+        if constexpr (MODE == kTensorwise) val[v] *= tscale;
+        if constexpr (!SPLIT) {
+          if (!GUARD || nq + v < p.N) val[v] += bias_at(p.bias, nq + v);
+        }
+      }
+      if (vec && (!GUARD || (m < p.M && nq + 3 < p.N))) {
+        if constexpr (SPLIT) {
+          *(float4*)(pbase + (int64_t)(m - pm0) * pld + (nq - pn0)) =
+              make_float4(val[0], val[1], val[2], val[3]);
+        } else if constexpr (OUT == kOutBf16) {
+          uint2 w;
+          w.x = f32_to_bf16_rne(val[0]) | (f32_to_bf16_rne(val[1]) << 16);
+          w.y = f32_to_bf16_rne(val[2]) | (f32_to_bf16_rne(val[3]) << 16);
+          *(uint2*)((uint16_t*)p.out + (int64_t)m * p.ldo + nq) = w;
+        } else {
+          *(float4*)((float*)p.out + (int64_t)m * p.ldo + nq) =
+              make_float4(val[0], val[1], val[2], val[3]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int n = nq + v;
+          if (!GUARD || (m < p.M && n < p.N)) {
+            if constexpr (SPLIT) {
+              pbase[(int64_t)(m - pm0) * pld + (n - pn0)] = val[v];
+            } else if constexpr (OUT == kOutBf16) {
+              ((uint16_t*)p.out)[(int64_t)m * p.ldo + n] = (uint16_t)f32_to_bf16_rne(val[v]);
+            } else {
+              ((float*)p.out)[(int64_t)m * p.ldo + n] = val[v];
+            }
           }
         }
       }
@@ -529,7 +562,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const uint32_t rbn_voff = (uint32_t)(min(n0 / 128 + lane, (p.N - 1) / 128) * p.rb_s_row * 4);
 
 #define FP8BW_ISSUE(kb, st)                                                                  \
-  issue_stage<AI, BI, RAI, RBI, RAB, RBB, NW, MODE>(p, (kb), sA[st], sB[st], sRa[st], sRb[st], \
+  issue_stage<AI, BI, RAI, RBI, RAB, RBB, NW, MODE, TM>(p, (kb), sA[st], sB[st], sRa[st], sRb[st], \
                                                     ars, brs, a_voff, b_voff, rbn_voff, wave, \
                                                     lane, m0, n0)
 
@@ -573,8 +606,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     uint32_t a_hi = (wm0 + frow) * 128 + (((2 * fhalf + 1) ^ swz(wm0 + frow)) << 4);
     uint32_t b_lo = (wn0 + frow) * 128 + (((2 * fhalf) ^ swz(wn0 + frow)) << 4);
     uint32_t b_hi = (wn0 + frow) * 128 + (((2 * fhalf + 1) ^ swz(wn0 + frow)) << 4);
-    uint32_t ra_off = (wm0 + 4 * fhalf) * 4;
-    uint32_t rb_off = (wn0 + frow) * 4;
+    uint32_t ra_off = (wm0 + TM * frow) * 4;
+    uint32_t rb_off = (wn0 + 4 * fhalf) * 4;
     asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(ra_off), "+v"(rb_off));
     const uint8_t* tA = sA[st];
     const uint8_t* tB = sB[st];
@@ -584,34 +617,44 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     v8i bf[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) bf[j] = load_frag_at(tB, b_lo + 2048 * j, b_hi + 2048 * j);
-    float sbn = 0.f;
-    float sbc[TN];
-    if constexpr (MODE == kBlockB128) sbn = sRb[st][(n0 + wn0) / 128 - n0 / 128];
-    if constexpr (MODE == kBlockB1x128) {
+    // Row scales of this lane's TM sub-tile rows (one row per sub-tile:
+    // the partials are computed transposed, see below), times the 128x128
+    // B scale of the wave's columns; per-row B scales of the lane's four
+    // columns of each column sub-tile.
+    float sa[TM];
+    v4f sbc[TN];
+    if constexpr (SCALED) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sbc[j] = *(const float*)(tRb + rb_off + 64 * j);
+      for (int q = 0; q < TM / 4; ++q) {
+        const v4f s4 = *(const v4f*)(tRa + ra_off + 16 * q);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sa[4 * q + v] = s4[v];
+      }
+      if constexpr (MODE == kBlockB128) {
+        const float sbn = sRb[st][(n0 + wn0) / 128 - n0 / 128];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa[i] *= sbn;
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sbc[j] = *(const v4f*)(tRb + rb_off + 64 * j);
+      }
     }
     // MFMA-granularity pipeline over the TM x TN sub-tiles (row-major): the
     // partial of sub-tile t lands in ring slot t % 3 and is folded into its
     // accumulator two MFMAs later, when it is complete, so each MFMA issues
-    // with the previous partials' rescale FMAs in its shadow.
+    // with the previous partials' rescale FMAs in its shadow.  The MFMA
+    // takes the B fragment as its first operand, so it computes the sub-tile
+    // transposed: lane l holds row 16 i + l % 16 and columns
+    // 16 j + 4 (l / 16) + v, one A row (one row scale) per lane.
     constexpr int T = TM * TN;
     // A rows are read PF rows ahead into a ring of PF + 1 fragment slots:
-    // row i + PF goes into the slot of row i - 1, its fragment as soon as row
-    // i starts (row i - 1's MFMAs are issued) and its scales one step later
-    // (after the last rescale of row i - 1 has read them).
+    // row i + PF goes into the slot of row i - 1 as soon as row i starts
+    // (row i - 1's MFMAs are issued).
     constexpr int PF = kRowPrefetch < TM ? kRowPrefetch : TM - 1;
     constexpr int NS = PF + 1;
     v8i af[NS];
-    v4f sa[NS];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      af[i] = load_frag_at(tA, a_lo + 2048 * i, a_hi + 2048 * i);
-      if constexpr (SCALED) {
-        sa[i] = *(const v4f*)(tRa + ra_off + 64 * i);
-        if constexpr (MODE == kBlockB128) sa[i] = sa[i] * sbn;
-      }
-    }
+    for (int i = 0; i < PF; ++i) af[i] = load_frag_at(tA, a_lo + 2048 * i, a_hi + 2048 * i);
     v4f ring[kRingDelay + 1];
 #pragma unroll
     for (int t = 0; t < T + kRingDelay; ++t) {
@@ -620,9 +663,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
         af[(i + PF) % NS] = load_frag_at(tA, a_lo + 2048 * (i + PF), a_hi + 2048 * (i + PF));
       if (t < T) {
         if (MODE == kTensorwise)
-          acc[i][j] = mfma_fp8(af[i % NS], bf[j], acc[i][j]);
+          acc[i][j] = mfma_fp8(bf[j], af[i % NS], acc[i][j]);
         else
-          ring[t % (kRingDelay + 1)] = mfma_fp8(af[i % NS], bf[j], v4f{0.f, 0.f, 0.f, 0.f});
+          ring[t % (kRingDelay + 1)] = mfma_fp8(bf[j], af[i % NS], v4f{0.f, 0.f, 0.f, 0.f});
       }
       if constexpr (SCALED) {
         if (t >= kRingDelay) {
@@ -630,14 +673,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             if constexpr (MODE == kBlockB128)
-              acc[iu][ju][v] = __builtin_fmaf(ring[u % (kRingDelay + 1)][v], sa[iu % NS][v], acc[iu][ju][v]);
+              acc[iu][ju][v] = __builtin_fmaf(ring[u % (kRingDelay + 1)][v], sa[iu], acc[iu][ju][v]);
             else
-              acc[iu][ju][v] = __builtin_fmaf(ring[u % (kRingDelay + 1)][v] * sbc[ju], sa[iu % NS][v], acc[iu][ju][v]);
+              acc[iu][ju][v] = __builtin_fmaf(ring[u % (kRingDelay + 1)][v] * sbc[ju][v], sa[iu],
+                                              acc[iu][ju][v]);
           }
-        }
-        if (t < T && j == 1 && i + PF < TM) {
-          sa[(i + PF) % NS] = *(const v4f*)(tRa + ra_off + 64 * (i + PF));
-          if constexpr (MODE == kBlockB128) sa[(i + PF) % NS] = sa[(i + PF) % NS] * sbn;
         }
       }
       // 128x128 B blocks: one MFMA, then the 4 rescale FMAs of an earlier
