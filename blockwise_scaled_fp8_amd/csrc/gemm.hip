@@ -497,14 +497,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int AOCT = BM / 8, BOCT = BN / 8;
-  static_assert(AOCT % NW == 0 && BOCT % NW == 0, "row octets must split evenly over waves");
-  constexpr int AI = AOCT / NW, BI = BOCT / NW;
+  // Waves that issue the direct loads.  Issuing a 1 KB direct load occupies
+  // the CU's vector memory address path for about 16 cycles, and a wave that
+  // issues a stage's loads stalls until they are taken in; with 8 waves only
+  // waves 0 and 1 issue them, so the other wave on their SIMD and both waves
+  // on the other SIMDs go straight to their MFMAs.
+  constexpr int LW = NW == 8 ? 2 : NW;
+  static_assert(AOCT % LW == 0 && BOCT % LW == 0, "row octets must split evenly over waves");
+  constexpr int AI = AOCT / LW, BI = BOCT / LW;
   constexpr bool SCALED = MODE != kTensorwise;
   constexpr int RAB = BM / 64;                       // 64-row blocks of ra
-  constexpr int RAI = SCALED ? (RAB + NW - 1) / NW : 0;
+  constexpr int RAI = SCALED ? (RAB + LW - 1) / LW : 0;
   constexpr int RBB = MODE == kBlockB1x128 ? BN / 64 : 1;
-  constexpr int RBI = SCALED ? (RBB + NW - 1) / NW : 0;
-  constexpr int LPS = AI + BI + RAI + RBI;           // loads per wave per stage
+  constexpr int RBI = SCALED ? (RBB + LW - 1) / LW : 0;
+  constexpr int LPS = AI + BI + RAI + RBI;           // loads per loading wave per stage
   constexpr int SBS = MODE == kBlockB1x128 ? BN : 64;
   static_assert(STAGES == 2 || STAGES == 3, "2 or 3 stages");
   static_assert(TN >= 2, "the rescale ring assumes at least two column sub-tiles");
@@ -547,8 +553,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   // 8q + c of a direct-load instruction fills physical chunk c of row 8o + q
   // (o = octet index), which holds logical chunk c ^ swz(8o + q); swz(8o + q)
   // = (4 (o & 1) + (q >> 1)) & 5 and o & 1 == wave & 1 because the octets of
-  // a wave step by NW (even).
-  static_assert(NW % 2 == 0, "octet parity must be the wave parity");
+  // a loading wave step by LW (even).
+  static_assert(LW % 2 == 0, "octet parity must be the wave parity");
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ ((4 * (wave & 1) + (lrow >> 1)) & 5);
   const uint32_t a_voff = (uint32_t)((8 * wave + lrow) * p.lda + lchunk * 16);
@@ -562,7 +568,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const uint32_t rbn_voff = (uint32_t)(min(n0 / 128 + lane, (p.N - 1) / 128) * p.rb_s_row * 4);
 
 #define FP8BW_ISSUE(kb, st)                                                                  \
-  issue_stage<AI, BI, RAI, RBI, RAB, RBB, NW, MODE, TM>(p, (kb), sA[st], sB[st], sRa[st], sRb[st], \
+  if (wave < LW)                                                                             \
+  issue_stage<AI, BI, RAI, RBI, RAB, RBB, LW, MODE, TM>(p, (kb), sA[st], sB[st], sRa[st], sRb[st], \
                                                     ars, brs, a_voff, b_voff, rbn_voff, wave, \
                                                     lane, m0, n0)
 
@@ -659,8 +666,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
 #pragma unroll
     for (int t = 0; t < T + kRingDelay; ++t) {
       const int i = t / TN, j = t % TN;
-      if (t < T && j == 0 && i + PF < TM)
+      if (t < T && j == 0 && i + PF < TM) {
         af[(i + PF) % NS] = load_frag_at(tA, a_lo + 2048 * (i + PF), a_hi + 2048 * (i + PF));
+        // Keep the read here, ahead of the row's MFMAs: left alone, the
+        // scheduler sinks it below them and reuses the current row's
+        // fragment registers, and every row then waits for its own read.
+        // (With per-row B scales the compiler's own order measured faster.)
+        if constexpr (MODE != kBlockB1x128) __builtin_amdgcn_sched_barrier(0);
+      }
       if (t < T) {
         if (MODE == kTensorwise)
           acc[i][j] = mfma_fp8(bf[j], af[i % NS], acc[i][j]);
