@@ -774,30 +774,59 @@ hipError_t launch_zero_bf16(void* out, int64_t rows, int64_t cols, hipStream_t s
 }
 
 // Sum tile-local split partials ([split][tile][BM][BN], grouped tile ids
-// tile_base ..) in split order and write the output tiles.
+// tile_base ..) in split order and write the output tiles.  One thread per
+// four consecutive columns of a tile row: 16-byte partial loads, one 8-byte
+// (bf16) or 16-byte (fp32) store where the output row allows it.  Indices
+// are 32-bit (the host keeps ntiles * BM * BN below 2^31).
 template <int BM, int BN, int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_tiled_kernel(
     const float* __restrict__ part, int splits, int ntiles, int tile_base, int tiles_m,
     int tiles_n, int M, int N, void* __restrict__ out, int64_t ldo,
     const uint16_t* __restrict__ bias) {
-  const int64_t per_tile = (int64_t)BM * BN;
-  const int64_t total = per_tile * ntiles;
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * 256) {
-    const int tl = (int)(idx / per_tile);
-    const int e = (int)(idx - (int64_t)tl * per_tile);
+  static_assert(BN % 4 == 0, "quads of columns");
+  constexpr int QPT = BM * BN / 4;   // quads per tile
+  const int total = BM * BN * ntiles;
+  const int nq = QPT * ntiles;
+  const bool vec = (ldo & 3) == 0 && ((size_t)out & 15) == 0;
+  for (int q = blockIdx.x * 256 + threadIdx.x; q < nq; q += gridDim.x * 256) {
+    const int tl = q / QPT;
+    const int e = (q - tl * QPT) * 4;
     const int r = e / BN, c = e - r * BN;
     int tm, tn;
     tile_to_mn(tile_base + tl, tiles_m, tiles_n, &tm, &tn);
     const int m = tm * BM + r, n = tn * BN + c;
     if (m >= M || n >= N) continue;
-    float s = 0.f;
-    for (int k = 0; k < splits; ++k) s += part[(int64_t)k * total + idx];
-    s += bias_at(bias, n);
-    if (OUT == kOutBf16)
-      ((uint16_t*)out)[(int64_t)m * ldo + n] = (uint16_t)f32_to_bf16_rne(s);
-    else
-      ((float*)out)[(int64_t)m * ldo + n] = s;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < splits; ++k) {
+      const float4 v = *(const float4*)(part + (int64_t)k * total + 4 * q);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    float val[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (n + v < N) val[v] += bias_at(bias, n + v);
+    if (vec && n + 3 < N) {
+      if (OUT == kOutBf16) {
+        uint2 w;
+        w.x = f32_to_bf16_rne(val[0]) | (f32_to_bf16_rne(val[1]) << 16);
+        w.y = f32_to_bf16_rne(val[2]) | (f32_to_bf16_rne(val[3]) << 16);
+        *(uint2*)((uint16_t*)out + (int64_t)m * ldo + n) = w;
+      } else {
+        *(float4*)((float*)out + (int64_t)m * ldo + n) = make_float4(val[0], val[1], val[2], val[3]);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (n + v >= N) break;
+        if (OUT == kOutBf16)
+          ((uint16_t*)out)[(int64_t)m * ldo + n + v] = (uint16_t)f32_to_bf16_rne(val[v]);
+        else
+          ((float*)out)[(int64_t)m * ldo + n + v] = val[v];
+      }
+    }
   }
 }
 
@@ -935,7 +964,8 @@ template <int BM, int BN>
 static hipError_t launch_tiled_reduce(const GemmArgs& a, int splits, int ntiles, int out_kind,
                                       hipStream_t stream) {
   const int64_t total = (int64_t)BM * BN * ntiles;
-  int64_t blocks = (total + 255) / 256;
+  if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // 32-bit indices
+  int64_t blocks = (total / 4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (out_kind == kOutBf16)
     hipLaunchKernelGGL((splitk_reduce_tiled_kernel<BM, BN, kOutBf16>), dim3((unsigned)blocks),
