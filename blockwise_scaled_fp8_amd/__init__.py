@@ -11,14 +11,17 @@ from .ops import (  # noqa: F401
     colmajor_empty,
     fp8_blockwise_quant,
     fp8_blockwise_quant_dual,
+    fp8_linear_bwd,
     fp8_linear_dgrad,
     fp8_linear_fwd,
+    fp8_linear_fwd_save,
     fp8_linear_wgrad,
     fp8_scaled_gemm_blockwise,
     fp8_scaled_gemm_tensorwise,
     fp8_scaled_grouped_gemm_blockwise,
     fp8_tensorwise_quant,
     fp8bw_gemm_num_configs,
+    linear_saved_bytes,
     linear_workspace,
     scale_grid,
 )

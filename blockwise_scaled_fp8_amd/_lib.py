@@ -49,6 +49,11 @@ PROTOTYPES = {
     "fp8_linear_fwd": (c_int, [c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_size, c_ptr]),
     "fp8_linear_dgrad": (c_int, [c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_size, c_ptr]),
     "fp8_linear_wgrad": (c_int, [c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_size, c_ptr]),
+    "fp8bw_linear_saved_bytes": (c_size, [c_i64, c_i64, c_i64]),
+    "fp8_linear_fwd_save": (c_int, [c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_size, c_ptr,
+                                    c_size, c_ptr]),
+    "fp8_linear_bwd": (c_int, [c_ptr, c_ptr, c_size, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr,
+                               c_size, c_ptr]),
 }
 
 STATUS = {0: "FP8BW_OK", 1: "FP8BW_ERR_NULL", 2: "FP8BW_ERR_SHAPE", 3: "FP8BW_ERR_LAYOUT",

@@ -413,6 +413,52 @@ struct LinearLayout {
   size_t a_codes, b_codes, a_recip, b_recip, gemm_ws, total;
 };
 
+// Fused-quantization wrapper (fp8_linear_fwd_save / fp8_linear_bwd).
+// Saved buffer: [W^T codes K x N][W^T recip cdiv(K,128) x cdiv(N,128)]
+//               [X^T codes K x M][X^T recip K x cdiv(M,128)]
+// fwd_save ws:  [X codes][W codes][X recip][W recip][fwd GEMM partials]
+// bwd ws:       [dY codes][dY^T codes][dY recip][dY^T recip][GEMM partials]
+struct SavedLayout {
+  size_t wt_codes, wt_recip, xt_codes, xt_recip, total;
+};
+
+SavedLayout saved_layout(int64_t M, int64_t N, int64_t K) {
+  SavedLayout S = {};
+  size_t off = 0;
+  S.wt_codes = off; off += align_up((size_t)(K * N));
+  S.wt_recip = off; off += align_up((size_t)(cdiv(K, 128) * cdiv(N, 128)) * 4);
+  S.xt_codes = off; off += align_up((size_t)(K * M));
+  S.xt_recip = off; off += align_up((size_t)(K * cdiv(M, 128)) * 4);
+  S.total = off;
+  return S;
+}
+
+struct FusedLayout {
+  size_t a_codes, a_codes_t, a_recip, a_recip_t, b_codes, b_recip, gemm_ws, total;
+};
+
+FusedLayout fused_layout(int64_t M, int64_t N, int64_t K, int which) {
+  FusedLayout F = {};
+  size_t off = 0;
+  if (which == 3) {   // fwd_save: X and W codes for the forward GEMM
+    F.a_codes = off; off += align_up((size_t)(M * K));
+    F.b_codes = off; off += align_up((size_t)(N * K));
+    F.a_recip = off; off += align_up((size_t)(M * cdiv(K, 128)) * 4);
+    F.b_recip = off; off += align_up((size_t)(cdiv(N, 128) * cdiv(K, 128)) * 4);
+    F.gemm_ws = off; off += align_up(fp8bw_gemm_blockwise_ws_bytes(M, N, K));
+  } else {            // bwd: dY and dY^T codes for dgrad and wgrad
+    F.a_codes = off; off += align_up((size_t)(M * N));
+    F.a_codes_t = off; off += align_up((size_t)(N * M));
+    F.a_recip = off; off += align_up((size_t)(M * cdiv(N, 128)) * 4);
+    F.a_recip_t = off; off += align_up((size_t)(N * cdiv(M, 128)) * 4);
+    F.gemm_ws = off;
+    const size_t g1 = fp8bw_gemm_blockwise_ws_bytes(M, K, N), g2 = fp8bw_gemm_blockwise_ws_bytes(N, K, M);
+    off += align_up(g1 > g2 ? g1 : g2);
+  }
+  F.total = off;
+  return F;
+}
+
 LinearLayout linear_layout(int64_t M, int64_t N, int64_t K, int which) {
   LinearLayout L = {};
   if (which == 0) { L.gm = M; L.gn = N; L.gk = K; }
@@ -451,8 +497,14 @@ int check_linear(const void* p0, const void* p1, void* out, int64_t M, int64_t N
 }  // namespace
 
 FP8BW_API size_t fp8bw_linear_ws_bytes(int64_t M, int64_t N, int64_t K, int which) {
-  if (which < 0 || which > 2 || M <= 0 || N <= 0 || K <= 0) return 0;
+  if (which < 0 || which > 4 || M <= 0 || N <= 0 || K <= 0) return 0;
+  if (which >= 3) return fused_layout(M, N, K, which).total;
   return linear_layout(M, N, K, which).total;
+}
+
+FP8BW_API size_t fp8bw_linear_saved_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return saved_layout(M, N, K).total;
 }
 
 static int zero_output(void* out, int64_t rows, int64_t cols, void* stream) {
@@ -520,4 +572,96 @@ FP8BW_API int fp8_linear_wgrad(const void* dy, const void* x, void* dw, int64_t 
   if ((st = fp8_blockwise_quant(x, M, K, K, FP8BW_BLOCK_1x128, 1, xtq, M, xtr, 1, K, stream))) return st;
   return fp8_scaled_gemm_blockwise(dytq, M, dytr, 1, N, xtq, M, xtr, 1, K, FP8BW_BLOCK_1x128, N, K, M,
                                    dw, K, FP8BW_OUT_BF16, base + L.gemm_ws, ws_bytes - L.gemm_ws, stream);
+}
+
+namespace {
+
+int check_fused(const void* p0, const void* p1, int64_t M, int64_t N, int64_t K, const void* saved,
+                size_t saved_bytes, void* ws, size_t ws_bytes, int which) {
+  if (M < 0 || N < 0 || K < 0) return fail(FP8BW_ERR_SHAPE, "negative dimension");
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(FP8BW_ERR_SHAPE, "dimension too large");
+  if (M % 16 || N % 16 || K % 16) return fail(FP8BW_ERR_SHAPE, "M, N, K must be multiples of 16");
+  if (which == 3 && K % 128) return fail(FP8BW_ERR_SHAPE, "K (%lld) must be a multiple of 128", (long long)K);
+  if (which == 4 && (M % 128 || N % 128))
+    return fail(FP8BW_ERR_SHAPE, "M (%lld) and N (%lld) must be multiples of 128", (long long)M, (long long)N);
+  if (M == 0 || N == 0 || K == 0) return FP8BW_OK;
+  if (!p0 || !p1 || !saved) return fail(FP8BW_ERR_NULL, "inputs and the saved buffer must be non-null");
+  if (!aligned(p0, 16) || !aligned(p1, 16)) return fail(FP8BW_ERR_ALIGN, "tensors must be 16-byte aligned");
+  const SavedLayout S = saved_layout(M, N, K);
+  if (saved_bytes < S.total) return fail(FP8BW_ERR_WORKSPACE, "saved buffer needs %zu bytes", S.total);
+  if (!aligned(saved, 256)) return fail(FP8BW_ERR_ALIGN, "saved must be 256-byte aligned");
+  const FusedLayout F = fused_layout(M, N, K, which);
+  if (!ws || ws_bytes < F.total) return fail(FP8BW_ERR_WORKSPACE, "workspace needs %zu bytes", F.total);
+  if (!aligned(ws, 256)) return fail(FP8BW_ERR_ALIGN, "ws must be 256-byte aligned");
+  return FP8BW_OK;
+}
+
+}  // namespace
+
+FP8BW_API int fp8_linear_fwd_save(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                                  int64_t K, void* saved, size_t saved_bytes, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  int st = check_fused(x, w, M, N, K, saved, saved_bytes, ws, ws_bytes, 3);
+  if (st != FP8BW_OK) return st;
+  if (M == 0 || N == 0 || K == 0) return ok();
+  if (!y) return fail(FP8BW_ERR_NULL, "y must be non-null");
+  if (!aligned(y, 16)) return fail(FP8BW_ERR_ALIGN, "y must be 16-byte aligned");
+  const SavedLayout S = saved_layout(M, N, K);
+  const FusedLayout F = fused_layout(M, N, K, 3);
+  uint8_t* base = (uint8_t*)ws;
+  uint8_t* sv = (uint8_t*)saved;
+  const int64_t nb = cdiv(N, 128), kbo = cdiv(K, 128);
+  uint8_t* xq = base + F.a_codes;
+  uint8_t* wq = base + F.b_codes;
+  float* xr = (float*)(base + F.a_recip);
+  float* wr = (float*)(base + F.b_recip);
+  // X: codes for the forward (1x128 along K, xr[m + kb*M]) and X^T for the
+  // weight gradient (1x128 along M, xtr[k + mb*K]) from one read.
+  if ((st = fp8_blockwise_quant_dual(x, M, K, K, FP8BW_BLOCK_1x128, xq, K, xr, 1, M, sv + S.xt_codes,
+                                     M, (float*)(sv + S.xt_recip), 1, K, stream)))
+    return st;
+  // W: 128x128 codes (wr[nb_i + kb*nb]) and W^T (wtr[kb_i + nb_i*kbo]).
+  if ((st = fp8_blockwise_quant_dual(w, N, K, K, FP8BW_BLOCK_128x128, wq, K, wr, 1, nb, sv + S.wt_codes,
+                                     N, (float*)(sv + S.wt_recip), 1, kbo, stream)))
+    return st;
+  return fp8_scaled_gemm_blockwise(xq, K, xr, 1, M, wq, K, wr, 1, nb, FP8BW_BLOCK_128x128, M, N, K,
+                                   y, N, FP8BW_OUT_BF16, base + F.gemm_ws, ws_bytes - F.gemm_ws, stream);
+}
+
+FP8BW_API int fp8_linear_bwd(const void* dy, const void* saved, size_t saved_bytes, void* dx,
+                             void* dw, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                             void* stream) {
+  int st = check_fused(dy, saved, M, N, K, saved, saved_bytes, ws, ws_bytes, 4);
+  if (st != FP8BW_OK) return st;
+  if (K == 0) return ok();
+  if (M == 0) return dw ? zero_output(dw, N, K, stream) : ok();
+  if (N == 0) return dx ? zero_output(dx, M, K, stream) : ok();
+  if ((dx && !aligned(dx, 16)) || (dw && !aligned(dw, 16)))
+    return fail(FP8BW_ERR_ALIGN, "dx and dw must be 16-byte aligned");
+  if (!dx && !dw) return ok();
+  const SavedLayout S = saved_layout(M, N, K);
+  const FusedLayout F = fused_layout(M, N, K, 4);
+  uint8_t* base = (uint8_t*)ws;
+  const uint8_t* sv = (const uint8_t*)saved;
+  const int64_t kbo = cdiv(K, 128);
+  uint8_t* dyq = base + F.a_codes;
+  uint8_t* dytq = base + F.a_codes_t;
+  float* dyr = (float*)(base + F.a_recip);
+  float* dytr = (float*)(base + F.a_recip_t);
+  // dY: 1x128 along N (dyr[m + nb*M]) for dgrad and 1x128 along M
+  // (dytr[n + mb*N]) for wgrad, from one read.
+  if ((st = fp8_blockwise_quant_dual(dy, M, N, N, FP8BW_BLOCK_1x128, dyq, N, dyr, 1, M, dytq, M,
+                                     dytr, 1, N, stream)))
+    return st;
+  if (dx && (st = fp8_scaled_gemm_blockwise(dyq, N, dyr, 1, M, sv + S.wt_codes, N,
+                                            (const float*)(sv + S.wt_recip), 1, kbo,
+                                            FP8BW_BLOCK_128x128, M, K, N, dx, K, FP8BW_OUT_BF16,
+                                            base + F.gemm_ws, ws_bytes - F.gemm_ws, stream)))
+    return st;
+  if (dw)
+    return fp8_scaled_gemm_blockwise(dytq, M, dytr, 1, N, sv + S.xt_codes, M,
+                                     (const float*)(sv + S.xt_recip), 1, K, FP8BW_BLOCK_1x128, N, K,
+                                     M, dw, K, FP8BW_OUT_BF16, base + F.gemm_ws,
+                                     ws_bytes - F.gemm_ws, stream);
+  return ok();
 }

@@ -248,6 +248,11 @@ def fp8_scaled_grouped_gemm_blockwise(a, ra, b, rb, group_end, out_dtype=torch.b
     return out
 
 
+def linear_saved_bytes(M, N, K):
+    """Bytes of the buffer fp8_linear_fwd_save fills for fp8_linear_bwd."""
+    return load_library().fp8bw_linear_saved_bytes(M, N, K)
+
+
 def linear_workspace(M, N, K, which, device):
     n = load_library().fp8bw_linear_ws_bytes(M, N, K, which)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
@@ -288,6 +293,50 @@ def fp8_linear_dgrad(dy, w, ws=None):
     K = w.shape[1]
     _check_shape(w, (N, K), "w")
     return _linear("fp8_linear_dgrad", 1, dy, w, (M, K), M, N, K, ws)
+
+
+def fp8_linear_fwd_save(x, w, ws=None):
+    """Y[M, N] = X . W^T with fused quantization: returns (Y, saved), where
+    saved (uint8, device) holds the X^T and W^T codes and scales that
+    fp8_linear_bwd needs (see include/fp8bw.h)."""
+    _bf16_2d(x, w)
+    M, K = x.shape
+    N = w.shape[0]
+    _check_shape(w, (N, K), "w")
+    lib = load_library()
+    _need_cuda(x, w)
+    if not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("linear inputs must be contiguous")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    saved = torch.empty(max(linear_saved_bytes(M, N, K), 1), dtype=torch.uint8, device=x.device)
+    if ws is None:
+        ws = linear_workspace(M, N, K, 3, x.device)
+    check(lib.fp8_linear_fwd_save(x.data_ptr(), w.data_ptr(), y.data_ptr(), M, N, K,
+                                  saved.data_ptr(), saved.numel(), ws.data_ptr(), ws.numel(),
+                                  _stream(x)))
+    return y, saved
+
+
+def fp8_linear_bwd(dy, saved, K, need_dx=True, need_dw=True, ws=None):
+    """(dX[M, K], dW[N, K]) from dY[M, N] and the saved buffer of
+    fp8_linear_fwd_save (dY quantized once); a gradient not needed is None."""
+    _bf16_2d(dy)
+    M, N = dy.shape
+    lib = load_library()
+    _need_cuda(dy, saved)
+    if not dy.is_contiguous():
+        raise ValueError("dy must be contiguous")
+    if saved.dtype != torch.uint8 or saved.dim() != 1:
+        raise ValueError("saved must be the 1-D uint8 buffer from fp8_linear_fwd_save")
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device) if need_dx else None
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device=dy.device) if need_dw else None
+    if ws is None:
+        ws = linear_workspace(M, N, K, 4, dy.device)
+    check(lib.fp8_linear_bwd(dy.data_ptr(), saved.data_ptr(), saved.numel(),
+                             dx.data_ptr() if dx is not None else None,
+                             dw.data_ptr() if dw is not None else None, M, N, K, ws.data_ptr(),
+                             ws.numel(), _stream(dy)))
+    return dx, dw
 
 
 def fp8_linear_wgrad(dy, x, ws=None):

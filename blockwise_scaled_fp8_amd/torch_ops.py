@@ -14,8 +14,13 @@ add bench script", Summary).  Here that is:
     its backward calls the dgrad and wgrad ops, each with the recipe the
     pages use for that GEMM (dY 1x128 x W^T 128x128; dY^T 1x128 x X^T 1x128
     along the token axis);
+  * ``torch.ops.fp8bw.linear_fwd_save`` / ``linear_bwd``: the same
+    computation with each bf16 tensor quantized once per step into both
+    code layouts (the forward keeps the X^T and W^T codes, the backward
+    quantizes dY once), bit-identical to the ops above;
   * ``Float8BlockwiseLinear``, a module with ``nn.Linear``'s interface
-    (bias-free) that flattens leading dimensions into the token axis.
+    (bias-free) that flattens leading dimensions into the token axis and
+    trains through the fused-quantization ops.
 
 Shapes follow the ABI's rules: in_features and out_features multiples of
 128 (they are contraction axes in fwd and dgrad) and a token count that is a
@@ -105,6 +110,62 @@ torch.library.register_autograd("fp8bw::linear", _linear_backward,
                                 setup_context=_linear_setup_context)
 
 
+@torch.library.custom_op("fp8bw::linear_fwd_save", mutates_args=())
+def linear_fwd_save(x: torch.Tensor, w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """(Y, saved): Y = X . W^T with X and W each quantized once into both
+    code layouts; saved holds the X^T and W^T codes and scales for
+    linear_bwd (one C-ABI call, fp8_linear_fwd_save)."""
+    _check_2d_bf16(x, w)
+    return ops.fp8_linear_fwd_save(x.contiguous(), w.contiguous())
+
+
+@linear_fwd_save.register_fake
+def _linear_fwd_save_fake(x, w):
+    _check_2d_bf16(x, w)
+    M, K = x.shape
+    N = w.shape[0]
+    n = max(ops.linear_saved_bytes(M, N, K), 1)
+    return x.new_empty((M, N)), x.new_empty((n,), dtype=torch.uint8)
+
+
+@torch.library.custom_op("fp8bw::linear_bwd", mutates_args=())
+def linear_bwd(dy: torch.Tensor, saved: torch.Tensor, k: int, need_dx: bool,
+               need_dw: bool) -> tuple[torch.Tensor, torch.Tensor]:
+    """(dX, dW) from dY (quantized once into both layouts) and the saved
+    buffer of linear_fwd_save; a gradient not asked for comes back empty."""
+    _check_2d_bf16(dy)
+    dx, dw = ops.fp8_linear_bwd(dy.contiguous(), saved, k, need_dx, need_dw)
+    return (dx if dx is not None else dy.new_empty((0,)),
+            dw if dw is not None else dy.new_empty((0,)))
+
+
+@linear_bwd.register_fake
+def _linear_bwd_fake(dy, saved, k, need_dx, need_dw):
+    _check_2d_bf16(dy)
+    M, N = dy.shape
+    return (dy.new_empty((M, k)) if need_dx else dy.new_empty((0,)),
+            dy.new_empty((N, k)) if need_dw else dy.new_empty((0,)))
+
+
+class _FusedQuantLinear(torch.autograd.Function):
+    """Y = X . W^T whose backward uses the transposed codes its forward
+    wrote (each bf16 tensor read once per training step)."""
+
+    @staticmethod
+    def forward(ctx, x, w):
+        y, saved = torch.ops.fp8bw.linear_fwd_save(x, w)
+        ctx.save_for_backward(saved)
+        ctx.k = x.shape[1]
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        (saved,) = ctx.saved_tensors
+        need_dx, need_dw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        dx, dw = torch.ops.fp8bw.linear_bwd(dy.contiguous(), saved, ctx.k, need_dx, need_dw)
+        return (dx if need_dx else None), (dw if need_dw else None)
+
+
 class Float8BlockwiseLinear(torch.nn.Module):
     """Bias-free ``nn.Linear`` counterpart whose forward and backward run the
     FP8 blockwise recipe: y = x W^T with x quantized per 1x128 and W per
@@ -145,7 +206,13 @@ class Float8BlockwiseLinear(torch.nn.Module):
 
     def forward(self, x):
         lead = x.shape[:-1]
-        y = torch.ops.fp8bw.linear(x.reshape(-1, self.in_features), self.weight)
+        x2 = x.reshape(-1, self.in_features)
+        if torch.is_grad_enabled() and (x.requires_grad or self.weight.requires_grad):
+            # Training: quantize X and W once into both layouts and keep the
+            # transposed fp8 codes (half the bytes of the bf16 X) for backward.
+            y = _FusedQuantLinear.apply(x2, self.weight)
+        else:
+            y = torch.ops.fp8bw.linear_fwd(x2, self.weight)
         return y.reshape(*lead, self.out_features)
 
     def extra_repr(self):

@@ -269,8 +269,8 @@ int fp8_scaled_gemm_tensorwise_bias(const void* a, int64_t lda, const float* ra,
  *   wgrad: dW[N, K] = dY^T . X  (dY^T, X^T 1x128 along M)   M % 128 == 0
  * Each quantizes its inputs into the caller's workspace (codes and
  * reciprocal scales) and runs the blockwise GEMM; bf16 output.
- * which = 0 fwd, 1 dgrad, 2 wgrad for the workspace query.  All dims must
- * also be multiples of 16.
+ * which = 0 fwd, 1 dgrad, 2 wgrad for the workspace query (3 and 4: the
+ * fused entry points below).  All dims must also be multiples of 16.
  */
 size_t fp8bw_linear_ws_bytes(int64_t M, int64_t N, int64_t K, int which);
 int fp8_linear_fwd(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
@@ -279,6 +279,35 @@ int fp8_linear_dgrad(const void* dy, const void* w, void* dx, int64_t M, int64_t
                      void* ws, size_t ws_bytes, void* stream);
 int fp8_linear_wgrad(const void* dy, const void* x, void* dw, int64_t M, int64_t N, int64_t K,
                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * FP8 blockwise linear with each bf16 tensor read once per step: the same
+ * three GEMMs and the same codes and scales as fp8_linear_fwd / _dgrad /
+ * _wgrad (bit-identical outputs), with fused quantization
+ * (fp8_blockwise_quant_dual): the forward quantizes X into X (1x128 along
+ * K) and X^T (1x128 along M), and W into W and W^T (128x128), keeping the
+ * transposed codes and scales for the backward; the backward quantizes dY
+ * once into dY and dY^T.  The quantizers are the part of the fp8 linear
+ * step the pages single out as slow ([INTEG] Benchmarks); fp8 X^T codes are
+ * also half the size of the bf16 X a backward would otherwise keep.
+ *
+ *   fp8_linear_fwd_save: Y[M, N] = X . W^T; writes `saved`.
+ *     Requires K % 128 == 0 (and M, N, K multiples of 16).
+ *   fp8_linear_bwd: dX[M, K] = dY . W and dW[N, K] = dY^T . X from dY and
+ *     the `saved` of the forward with the same X, W, M, N, K.  dx or dw may
+ *     be null to skip that gradient.  Requires M % 128 == 0 and N % 128 == 0.
+ *   saved   caller device memory of fp8bw_linear_saved_bytes(M, N, K)
+ *           bytes, 256-byte aligned, owned by the caller between the two
+ *           calls; its layout is internal to the library.
+ *   ws      workspace of fp8bw_linear_ws_bytes(M, N, K, which) bytes with
+ *           which = 3 (fwd_save) or 4 (bwd), 256-byte aligned.
+ * Errors as for fp8_linear_fwd; nothing is launched on an error.
+ */
+size_t fp8bw_linear_saved_bytes(int64_t M, int64_t N, int64_t K);
+int fp8_linear_fwd_save(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                        void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+int fp8_linear_bwd(const void* dy, const void* saved, size_t saved_bytes, void* dx, void* dw,
+                   int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -200,6 +200,32 @@ def test_linear_validation_and_workspace(lib):
     assert lib.fp8_linear_wgrad(P, P, P, 144, 256, 256, P, 1 << 24, None) == SHAPE
 
 
+def test_fused_linear_validation_and_buffers(lib):
+    """fp8_linear_fwd_save / fp8_linear_bwd reject bad shapes, buffers and
+    alignment before launching anything."""
+    M = N = K = 256
+    saved = lib.fp8bw_linear_saved_bytes(M, N, K)
+    assert saved >= 2 * 256 * 256                      # X^T and W^T codes at least
+    assert lib.fp8bw_linear_saved_bytes(0, N, K) == 0
+    need_f = lib.fp8bw_linear_ws_bytes(M, N, K, 3)
+    need_b = lib.fp8bw_linear_ws_bytes(M, N, K, 4)
+    assert need_f >= 2 * 256 * 256 and need_b >= 2 * 256 * 256
+    assert lib.fp8bw_linear_ws_bytes(M, N, K, 5) == 0
+    f, b = lib.fp8_linear_fwd_save, lib.fp8_linear_bwd
+    assert f(P, P, P, M, N, K, P, saved - 1, P, need_f, None) == WS           # saved too small
+    assert f(P, P, P, M, N, K, P, saved, P, need_f - 1, None) == WS           # ws too small
+    assert f(P, P, P, M, N, K, None, saved, P, need_f, None) == NULL
+    assert f(None, P, P, M, N, K, P, saved, P, need_f, None) == NULL
+    assert f(P, P, P, M, N, 144, P, 1 << 24, P, 1 << 26, None) == SHAPE       # K % 128
+    assert f(P, P, P, M, N, K, P + 16, saved, P, need_f, None) == ALIGN       # saved 256-aligned
+    assert b(P, P, saved, P, P, M, N, K, P, need_b - 1, None) == WS
+    assert b(P, P, saved - 1, P, P, M, N, K, P, need_b, None) == WS
+    assert b(P, None, saved, P, P, M, N, K, P, need_b, None) == NULL
+    assert b(P, P, 1 << 24, P, P, 144, N, K, P, 1 << 26, None) == SHAPE       # M % 128
+    assert b(P, P, 1 << 24, P, P, M, 144, K, P, 1 << 26, None) == SHAPE       # N % 128
+    assert b(P, P, saved, P + 4, P, M, N, K, P, need_b, None) == ALIGN        # dx 16-aligned
+
+
 def test_binding_raises_with_message(lib):
     st = _gemm(lib, K=200)
     with pytest.raises(fp8.FP8BWError, match="K % 128"):

@@ -116,3 +116,28 @@ def test_linear_shared_workspace_reuse(gpu):
             (dx, linear.dgrad(bits(dy), bits(w), True), N // 128, "dgrad"),
             (dw, linear.wgrad(bits(dy), bits(x), True), M // 128, "wgrad")):
         check_gemm_output(host_f32(got), ref, S, kb, "bf16", name)
+
+
+@pytest.mark.parametrize("mnk", [(384, 256, 640), (16640, 5120, 8192)])
+def test_fused_quant_linear_matches_separate(gpu, mnk):
+    """fp8_linear_fwd_save + fp8_linear_bwd (each bf16 tensor quantized once
+    into both layouts) give bit-identical Y, dX and dW to the three separate
+    entry points, whose results the tests above check against the oracle;
+    a skipped gradient leaves the other unchanged."""
+    M, N, K = mnk
+    say("fused linear", mnk)
+    x, w, dy = _inputs(M, N, K, seed=5, device=gpu)
+    y_ref = fp8.fp8_linear_fwd(x, w)
+    dx_ref = fp8.fp8_linear_dgrad(dy, w)
+    dw_ref = fp8.fp8_linear_wgrad(dy, x)
+    y, saved = fp8.fp8_linear_fwd_save(x, w)
+    dx, dw = fp8.fp8_linear_bwd(dy, saved, K)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref), "fused fwd differs from fp8_linear_fwd"
+    assert torch.equal(dx, dx_ref), "fused dgrad differs from fp8_linear_dgrad"
+    assert torch.equal(dw, dw_ref), "fused wgrad differs from fp8_linear_wgrad"
+    dx2, none_dw = fp8.fp8_linear_bwd(dy, saved, K, need_dx=True, need_dw=False)
+    none_dx, dw2 = fp8.fp8_linear_bwd(dy, saved, K, need_dx=False, need_dw=True)
+    torch.cuda.synchronize()
+    assert none_dw is None and none_dx is None
+    assert torch.equal(dx2, dx_ref) and torch.equal(dw2, dw_ref)

@@ -13,7 +13,8 @@ def _meta(*shape, grad=False):
 
 
 def test_ops_registered():
-    for name in ("linear", "linear_fwd", "linear_dgrad", "linear_wgrad"):
+    for name in ("linear", "linear_fwd", "linear_dgrad", "linear_wgrad", "linear_fwd_save",
+                 "linear_bwd"):
         assert hasattr(torch.ops.fp8bw, name)
 
 
@@ -25,6 +26,17 @@ def test_fake_shapes():
     assert torch.ops.fp8bw.linear_wgrad(dy, x).shape == (384, 512)
     with pytest.raises(ValueError):
         torch.ops.fp8bw.linear_fwd(x.float(), w)
+
+
+def test_fused_fake_shapes():
+    x, w, dy = _meta(256, 512), _meta(384, 512), _meta(256, 384)
+    y, saved = torch.ops.fp8bw.linear_fwd_save(x, w)
+    assert y.shape == (256, 384) and saved.dtype == torch.uint8 and saved.dim() == 1
+    assert saved.numel() == fp8.linear_saved_bytes(256, 384, 512)
+    dx, dw = torch.ops.fp8bw.linear_bwd(dy, saved, 512, True, True)
+    assert dx.shape == (256, 512) and dw.shape == (384, 512)
+    dx, dw = torch.ops.fp8bw.linear_bwd(dy, saved, 512, False, True)
+    assert dx.numel() == 0 and dw.shape == (384, 512)
 
 
 def test_module_autograd_shapes_on_meta():
