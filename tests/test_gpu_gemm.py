@@ -226,30 +226,51 @@ def test_gemm_deterministic(gpu):
     assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
 
 
-def test_tail_split_of_last_round():
+@pytest.mark.parametrize("mode,od", [("128x128", "f32"), ("128x128", "bf16"), ("1x128", "f32"),
+                                     ("1x128", "bf16"), ("tensorwise", "f32"),
+                                     ("tensorwise", "bf16")])
+def test_tail_split_of_last_round(mode, od):
     """272 tiles of 256x256 on 256 CUs: the leftover 16 tiles (the last
-    row-block of tiles in the grouped order) run split-K into tile-local
-    partials.  Rows of that block and random others match the oracle, and
-    the split and unsplit runs agree within the fp32 rounding bound."""
+    row-block of tiles in the grouped order) run split over K into
+    tile-local partials after the 256 whole tiles, then an ordered reduce.
+    Rows of that block and random others match the oracle for every scale
+    mode and output type, and so does the plan forced to one unsplit
+    launch; rows of whole tiles are identical in both runs."""
     import torch as _t
     dev = _t.device("cuda", 0)
     rng = np.random.default_rng(40)
     M, N, K = 4352, 4096, 2048
     aq = _random_codes(rng, (M, K))
     bq = _random_codes(rng, (N, K))
+    dt = _t.bfloat16 if od == "bf16" else _t.float32
+    rows = np.unique(np.r_[np.arange(M - 256, M, 3), rng.choice(M - 256, 32, replace=False)])
+    if mode == "tensorwise":
+        ar, br = np.float32(1.5e-3), np.float32(1.25e-3)
+        say("gemm tail split tensorwise", od)
+        auto = fp8.fp8_scaled_gemm_tensorwise(_up_codes(aq, dev), _t.tensor([ar], device=dev),
+                                              _up_codes(bq, dev), _t.tensor([br], device=dev),
+                                              out_dtype=dt)
+        _t.cuda.synchronize()
+        ref = gemm.tensorwise_gemm(aq[rows], ar, bq, br)
+        S = gemm.tensorwise_bound(aq[rows], ar, bq, br)
+        check_gemm_output(host_f32(auto)[rows], ref, S, K // 128, od, f"tail split tensorwise {od}")
+        return
     ar = rng.uniform(1e-3, 2e-3, (M, K // 128)).astype(np.float32)
-    br = rng.uniform(1e-3, 2e-3, (N // 128, K // 128)).astype(np.float32)
+    nb = N if mode == "1x128" else N // 128
+    br = rng.uniform(1e-3, 2e-3, (nb, K // 128)).astype(np.float32)
     args = (_up_codes(aq, dev), _up_scales_colmajor(ar, dev), _up_codes(bq, dev),
             _up_scales_colmajor(br, dev))
-    say("gemm tail split auto")
-    auto = fp8.fp8_scaled_gemm_blockwise(*args, out_dtype=_t.float32)
-    say("gemm tail split forced off")
-    plain = fp8.fp8_scaled_gemm_blockwise(*args, out_dtype=_t.float32, config=3, splits=1)
+    say("gemm tail split auto", mode, od)
+    auto = fp8.fp8_scaled_gemm_blockwise(*args, b_block=mode, out_dtype=dt)
+    say("gemm tail split forced off", mode, od)
+    plain = fp8.fp8_scaled_gemm_blockwise(*args, b_block=mode, out_dtype=dt, config=3, splits=1)
     _t.cuda.synchronize()
-    rows = np.unique(np.r_[np.arange(M - 256, M, 3), rng.choice(M - 256, 32, replace=False)])
-    ref, S = gemm.blockwise_gemm(aq[rows], ar[rows], bq, br, "128x128", with_bound=True)
+    ref, S = gemm.blockwise_gemm(aq[rows], ar[rows], bq, br, mode, with_bound=True)
     for name, out in (("auto", auto), ("plain", plain)):
-        check_gemm_output(host_f32(out)[rows], ref, S, K // 128, "f32", f"tail split {name}")
+        check_gemm_output(host_f32(out)[rows], ref, S, K // 128, od, f"tail split {name} {mode}")
+    # rows outside the leftover block come from whole tiles in both runs
+    whole = host_f32(auto)[: M - 256]
+    assert np.array_equal(whole, host_f32(plain)[: M - 256])
 
 
 @pytest.mark.parametrize("mnk,b_block,od", [
