@@ -27,7 +27,8 @@ bounded sample of the same workload.  Also reported: `separate_quant_step`,
 the same step with the six separate quantizer launches of fp8_linear_fwd /
 _dgrad / _wgrad (X and dY each read twice), `grouped_gemm`, the
 mixture-of-experts grouped GEMM at the forward shape, and
-`quant_standalone`, the quantizers alone on a 32768^2 input.
+`quant_standalone`, the quantizers alone on S x S inputs, S = 1024 .. 32768
+(headline entries at 32768^2).
 """
 
 import argparse
@@ -172,39 +173,59 @@ def run_gpu(steps, warmup, seed, plan_fn=None, wl=None):
             "quant_gbps": qbytes / (qms * 1e-3) / 1e9, "quant_us": qms * 1e3, "workload": wl}
 
 
-def quant_standalone(seed, size=32768, reps=10):
-    """The quantizers alone on one square bf16 input far larger than the
-    256 MB Infinity Cache (32768^2: 2 GiB in, 1 GiB of codes out), both block
-    shapes, HIP events around each call on the launch stream.  Algorithmic
-    bytes as in the step (2 B read + 1 B written per element + 4 B per
-    scale)."""
+def _time_quant(xs, qs, recips, block, reps):
+    """Average duration (ms) of one quantizer call, cycling through the
+    buffers so consecutive calls touch different memory; one HIP event pair
+    around the whole sequence on the launch stream."""
     import blockwise_scaled_fp8_amd as fp8
+    n = len(xs)
+    for i in range(min(n, 3)):
+        fp8.fp8_blockwise_quant(xs[i], block, q=qs[i], recip=recips[i])
+    torch.cuda.synchronize()
+    calls = max(reps, 2 * n)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(calls):
+        fp8.fp8_blockwise_quant(xs[i % n], block, q=qs[i % n], recip=recips[i % n])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / calls
+
+
+def quant_standalone(seed, sizes=(1024, 2048, 4096, 8192, 16384, 32768), reps=10,
+                     rotate_bytes=1 << 30):
+    """The quantizers alone on square S x S bf16 inputs, both block shapes.
+    Each size cycles through enough input / output buffer sets that their
+    inputs total at least 1 GiB, four times the 256 MB Infinity Cache, so
+    every call streams from HBM (32768^2 is one 2 GiB input).  Algorithmic bytes as
+    in the step (2 B read + 1 B written per element + 4 B per scale).  The
+    headline entries are the 32768^2 ones; small sizes are launch-bound."""
     from synth import inputs
     dev = torch.device("cuda", 0)
-    x = inputs.randn_bf16((size, size), seed=inputs.tensor_seed(seed, "a"), device=dev)
-    q = torch.empty(size, size, dtype=torch.uint8, device=dev)
-    res = {}
-    for block in ("1x128", "128x128"):
-        nkb = cdiv(size, 128)
-        rows = size if block == "1x128" else cdiv(size, 128)
-        recip = torch.empty(nkb, rows, dtype=torch.float32, device=dev).t()
-        for _ in range(3):
-            fp8.fp8_blockwise_quant(x, block, q=q, recip=recip)
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        evs[0].record(stream)
-        for i in range(reps):
-            fp8.fp8_blockwise_quant(x, block, q=q, recip=recip)
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(reps)) / reps
-        gbps = quant_bytes(size, size, block) / (ms * 1e-3) / 1e9
-        res[block] = {"avg_us": round(ms * 1e3, 1), "gbps": round(gbps, 1),
-                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)}
-    del x, q
-    torch.cuda.empty_cache()
-    return {"shape": [size, size], **res}
+    sweep = {}
+    for size in sizes:
+        nbuf = max(1, cdiv(rotate_bytes, 2 * size * size))
+        x0 = inputs.randn_bf16((size, size), seed=inputs.tensor_seed(seed, "a"), device=dev)
+        xs = [x0] + [x0.clone() for _ in range(nbuf - 1)]
+        qs = [torch.empty(size, size, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        entry = {"buffers": nbuf}
+        for block in ("1x128", "128x128"):
+            nkb = cdiv(size, 128)
+            rows = size if block == "1x128" else cdiv(size, 128)
+            recips = [torch.empty(nkb, rows, dtype=torch.float32, device=dev).t() for _ in range(nbuf)]
+            ms = _time_quant(xs, qs, recips, block, reps)
+            gbps = quant_bytes(size, size, block) / (ms * 1e-3) / 1e9
+            entry[block] = {"avg_us": round(ms * 1e3, 2), "gbps": round(gbps, 1),
+                            "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)}
+            del recips
+        sweep[str(size)] = entry
+        del xs, qs, x0
+        torch.cuda.empty_cache()
+    top = sweep[str(max(sizes))]
+    return {"shape": [max(sizes), max(sizes)], "1x128": top["1x128"], "128x128": top["128x128"],
+            "sweep": sweep}
 
 
 def grouped_gemm(seed, wl, groups=8, reps=10):
