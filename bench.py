@@ -23,12 +23,16 @@ Prints one JSON line: `value` is the step's effective throughput,
 3 * 2MNK flops / step time (TFLOP/s); `roofline` is for the dominant kernel,
 the forward blockwise GEMM (2MNK flops per launch / its average duration vs
 the 5.0 PFLOP/s dense FP8 peak); `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.  Also reported: `separate_quant_step`,
-the same step with the six separate quantizer launches of fp8_linear_fwd /
-_dgrad / _wgrad (X and dY each read twice), `grouped_gemm`, the
-mixture-of-experts grouped GEMM at the forward shape, and
-`quant_standalone`, the quantizers alone on S x S inputs, S = 1024 .. 32768
-(headline entries at 32768^2).
+bounded sample of the same workload.  Also reported:
+  separate_quant_step   the same step with the six separate quantizer
+                        launches of fp8_linear_fwd / _dgrad / _wgrad (X and
+                        dY each read twice);
+  step_16640x8192x5120  the fused step at the second linear shape (N and K
+                        swapped);
+  grouped_gemm          the mixture-of-experts grouped GEMM at the forward
+                        shape;
+  quant_standalone      the quantizers alone on S x S inputs, S = 1024 ..
+                        32768 (headline entries at 32768^2).
 """
 
 import argparse
@@ -46,6 +50,7 @@ METRIC = "blockwise FP8 GEMM TFLOP/s (M16640 N5120 K8192) + quant GB/s, 1 MI355X
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (no sparsity)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 M, N, K = 16640, 5120, 8192
+SHAPE2 = (16640, 8192, 5120)
 
 
 def cdiv(a, b):
@@ -53,10 +58,12 @@ def cdiv(a, b):
 
 
 class Workload:
-    """Inputs, codes, scales and outputs of one linear step, all in HBM."""
+    """Inputs, codes, scales and outputs of one linear step, all in HBM
+    (X [M, K], W [N, K], dY [M, N])."""
 
-    def __init__(self, seed, dev):
+    def __init__(self, seed, dev, shape=(M, N, K)):
         from synth import inputs
+        M, N, K = self.M, self.N, self.K = shape
         self.x = inputs.randn_bf16((M, K), seed=inputs.tensor_seed(seed, "x"), device=dev)
         self.w = inputs.linear_weight_bf16(N, K, seed=inputs.tensor_seed(seed, "w"), device=dev)
         self.dy = inputs.randn_bf16((M, N), seed=inputs.tensor_seed(seed, "dy"), device=dev)
@@ -85,6 +92,7 @@ def step_plan(wl):
     import blockwise_scaled_fp8_amd as fp8
     q = fp8.fp8_blockwise_quant
     g = fp8.fp8_scaled_gemm_blockwise
+    M, N, K = wl.M, wl.N, wl.K
     return [
         ("quant_1x128 X", lambda: q(wl.x, "1x128", q=wl.xq, recip=wl.xr),
          quant_bytes(M, K, "1x128"), "B"),
@@ -115,6 +123,7 @@ def step_plan_dual(wl):
     import blockwise_scaled_fp8_amd as fp8
     d = fp8.fp8_blockwise_quant_dual
     g = fp8.fp8_scaled_gemm_blockwise
+    M, N, K = wl.M, wl.N, wl.K
     return [
         ("quant_dual X", lambda: d(wl.x, "1x128", q=wl.xq, recip=wl.xr, qt=wl.xtq, recip_t=wl.xtr),
          2 * M * K + 2 * M * K + 4 * (M * cdiv(K, 128) + K * cdiv(M, 128)), "B"),
@@ -131,13 +140,13 @@ def step_plan_dual(wl):
     ]
 
 
-def run_gpu(steps, warmup, seed, plan_fn=None, wl=None):
+def run_gpu(steps, warmup, seed, plan_fn=None, wl=None, shape=(M, N, K)):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     import blockwise_scaled_fp8_amd as fp8
     fp8.load_library()
     if wl is None:
-        wl = Workload(seed, dev)
+        wl = Workload(seed, dev, shape)
     plan = (plan_fn or step_plan)(wl)
     torch.cuda.synchronize()
     for _ in range(warmup):
@@ -410,6 +419,17 @@ def main():
             "kernels": rd["kernels"]}
         out["grouped_gemm"] = grouped_gemm(args.seed, r["workload"])
     del r, rd
+    if not args.step_only:
+        # the second linear shape of the workload (N and K swapped)
+        r2 = run_gpu(args.steps, args.warmup, args.seed, plan_fn=step_plan_dual, shape=SHAPE2)
+        m2, n2, k2 = SHAPE2
+        out["step_%dx%dx%d" % SHAPE2] = {
+            "M": m2, "N": n2, "K": k2,
+            "ms_per_step": round(r2["gpu_ms_per_step"], 4),
+            "value": round(3 * 2 * m2 * n2 * k2 / (r2["gpu_ms_per_step"] * 1e-3) / 1e12, 1),
+            "gemm_tflops": {k: v["tflops"] for k, v in r2["kernels"].items() if "tflops" in v},
+            "quant_gbps": round(r2["quant_gbps"], 1)}
+        del r2
     if not args.no_quant_standalone:
         out["quant_standalone"] = quant_standalone(args.seed)
     if args.copy_probe_gib > 0:
