@@ -28,6 +28,8 @@
 //  * Split-K writes fp32 partials [split, M, N]; a separate kernel sums them
 //    in split order (deterministic, no atomics).
 
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -862,23 +864,25 @@ bool gemm_config_ok(const GemmProblem& p, int cfg) {
 
 // Compute units of the current device (the number of workgroups that run
 // concurrently with one large-tile workgroup per CU); 256 when unknown.
+// Cached per device; calls from several host threads may race to fill an
+// entry, all with the same value, hence the relaxed atomics.
 static int num_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
     return 256;
   }
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0) {
       (void)hipGetLastError();
       n = 256;
     }
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 static int heuristic_config(const GemmProblem& p) {

@@ -4,6 +4,8 @@ outputs with torch (device memory is plumbing), passes raw pointers, sizes and
 the current HIP stream, and raises FP8BWError on a non-OK status.  Every step
 of the computation runs in the HIP kernels of libfp8bw.so."""
 
+import functools
+
 import torch
 
 from ._lib import check, load_library
@@ -20,6 +22,30 @@ def _need_cuda(*ts):
     for t in ts:
         if not (isinstance(t, torch.Tensor) and t.is_cuda):
             raise ValueError("fp8bw ops take CUDA (HIP) tensors")
+
+
+def _on_tensor_device(fn):
+    """Every tensor argument (inputs and caller-provided outputs or
+    workspace) must be a HIP tensor on one device; that device is made
+    current for the call, so the library's launches, its per-device queries
+    and the stream all refer to the device that holds the data."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        dev = None
+        for t in list(args) + list(kwargs.values()):
+            if not isinstance(t, torch.Tensor):
+                continue
+            if not t.is_cuda:
+                raise ValueError("fp8bw ops take CUDA (HIP) tensors")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"fp8bw ops take tensors on one device ({dev} and {t.device} given)")
+        if dev is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.device(dev):
+            return fn(*args, **kwargs)
+    return wrapper
 
 
 def _rowmajor(t, name):
@@ -56,6 +82,7 @@ def _check_shape(t, shape, name):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+@_on_tensor_device
 def fp8_blockwise_quant(x, block="1x128", transpose=False, q=None, recip=None):
     """Quantize bf16 x[rows, cols] to E4M3 codes with per-block reciprocal scales.
 
@@ -81,6 +108,7 @@ def fp8_blockwise_quant(x, block="1x128", transpose=False, q=None, recip=None):
     return q, recip
 
 
+@_on_tensor_device
 def fp8_blockwise_quant_dual(x, block="1x128", q=None, recip=None, qt=None, recip_t=None):
     """Both layouts from one read of x: returns (q, recip, qt, recip_t), equal
     to fp8_blockwise_quant(x, block) and fp8_blockwise_quant(x, block,
@@ -113,6 +141,7 @@ def fp8_blockwise_quant_dual(x, block="1x128", q=None, recip=None, qt=None, reci
     return q, recip, qt, recip_t
 
 
+@_on_tensor_device
 def fp8_tensorwise_quant(x, q=None, recip=None):
     """Per-tensor quantization: (q uint8 like x, recip fp32 [1] on device)."""
     lib = load_library()
@@ -139,6 +168,7 @@ def _check_bias(bias, N, device):
         raise ValueError("bias must be on the GEMM's device")
 
 
+@_on_tensor_device
 def fp8_scaled_gemm_blockwise(a, ra, b, rb, b_block="128x128", out_dtype=torch.bfloat16,
                               out=None, config=None, splits=None, bias=None):
     """out[M, N] = blockwise-scaled A . B^T (see include/fp8bw.h).
@@ -191,6 +221,7 @@ def fp8bw_gemm_num_configs():
     return load_library().fp8bw_gemm_num_configs()
 
 
+@_on_tensor_device
 def fp8_scaled_gemm_tensorwise(a, ra, b, rb, out_dtype=torch.bfloat16, out=None, bias=None):
     """out[M, N] = (A . B^T) * ra * rb with one-element device scales."""
     lib = load_library()
@@ -218,6 +249,7 @@ def fp8_scaled_gemm_tensorwise(a, ra, b, rb, out_dtype=torch.bfloat16, out=None,
     return out
 
 
+@_on_tensor_device
 def fp8_scaled_grouped_gemm_blockwise(a, ra, b, rb, group_end, out_dtype=torch.bfloat16, out=None):
     """Grouped blockwise GEMM: rows [group_end[g-1], group_end[g]) of a
     (uint8 [M, K], ra fp32 [M, K/128] column-major) times b[g]^T (uint8
@@ -277,6 +309,7 @@ def _bf16_2d(*ts):
             raise ValueError("linear inputs are 2-D bf16 tensors")
 
 
+@_on_tensor_device
 def fp8_linear_fwd(x, w, ws=None):
     """Y[M, N] = X . W^T (X 1x128, W 128x128), bf16."""
     _bf16_2d(x, w)
@@ -286,6 +319,7 @@ def fp8_linear_fwd(x, w, ws=None):
     return _linear("fp8_linear_fwd", 0, x, w, (M, N), M, N, K, ws)
 
 
+@_on_tensor_device
 def fp8_linear_dgrad(dy, w, ws=None):
     """dX[M, K] = dY . W (dY 1x128, W^T 128x128), bf16."""
     _bf16_2d(dy, w)
@@ -295,6 +329,7 @@ def fp8_linear_dgrad(dy, w, ws=None):
     return _linear("fp8_linear_dgrad", 1, dy, w, (M, K), M, N, K, ws)
 
 
+@_on_tensor_device
 def fp8_linear_fwd_save(x, w, ws=None):
     """Y[M, N] = X . W^T with fused quantization: returns (Y, saved), where
     saved (uint8, device) holds the X^T and W^T codes and scales that
@@ -317,6 +352,7 @@ def fp8_linear_fwd_save(x, w, ws=None):
     return y, saved
 
 
+@_on_tensor_device
 def fp8_linear_bwd(dy, saved, K, need_dx=True, need_dw=True, ws=None):
     """(dX[M, K], dW[N, K]) from dY[M, N] and the saved buffer of
     fp8_linear_fwd_save (dY quantized once); a gradient not needed is None."""
@@ -339,6 +375,7 @@ def fp8_linear_bwd(dy, saved, K, need_dx=True, need_dw=True, ws=None):
     return dx, dw
 
 
+@_on_tensor_device
 def fp8_linear_wgrad(dy, x, ws=None):
     """dW[N, K] = dY^T . X (1x128 x 1x128 along M), bf16."""
     _bf16_2d(dy, x)
