@@ -118,7 +118,7 @@ def test_linear_shared_workspace_reuse(gpu):
         check_gemm_output(host_f32(got), ref, S, kb, "bf16", name)
 
 
-@pytest.mark.parametrize("mnk", [(384, 256, 640), (16640, 5120, 8192)])
+@pytest.mark.parametrize("mnk", [(384, 256, 640), (16640, 5120, 8192), (16640, 8192, 5120)])
 def test_fused_quant_linear_matches_separate(gpu, mnk):
     """fp8_linear_fwd_save + fp8_linear_bwd (each bf16 tensor quantized once
     into both layouts) give bit-identical Y, dX and dW to the three separate
