@@ -141,3 +141,40 @@ def test_fused_quant_linear_matches_separate(gpu, mnk):
     torch.cuda.synchronize()
     assert none_dw is None and none_dx is None
     assert torch.equal(dx2, dx_ref) and torch.equal(dw2, dw_ref)
+
+
+def test_fused_linear_canaries(gpu):
+    """fp8_linear_fwd_save / fp8_linear_bwd through the C ABI with the saved
+    buffer, the workspaces and the outputs placed in canary-filled buffers
+    larger than the sizes passed: nothing past the stated sizes is written,
+    and the results equal the binding's bit for bit."""
+    from blockwise_scaled_fp8_amd._lib import check
+    lib = fp8.load_library()
+    M, N, K = 384, 256, 640
+    x, w, dy = (t.to(gpu) for t in _inputs(M, N, K, seed=9, device="cpu"))
+    pad = 4096
+    saved_bytes = lib.fp8bw_linear_saved_bytes(M, N, K)
+    ws_f, ws_b = lib.fp8bw_linear_ws_bytes(M, N, K, 3), lib.fp8bw_linear_ws_bytes(M, N, K, 4)
+    canary = 0xA5
+
+    def u8(n):
+        return torch.full((n + pad,), canary, dtype=torch.uint8, device=gpu)
+
+    saved, wsf, wsb = u8(saved_bytes), u8(ws_f), u8(ws_b)
+    yb, dxb, dwb = u8(2 * M * N), u8(2 * M * K), u8(2 * N * K)
+    stream = torch.cuda.current_stream().cuda_stream
+    say("fused linear canaries")
+    check(lib.fp8_linear_fwd_save(x.data_ptr(), w.data_ptr(), yb.data_ptr(), M, N, K,
+                                  saved.data_ptr(), saved_bytes, wsf.data_ptr(), ws_f, stream))
+    check(lib.fp8_linear_bwd(dy.data_ptr(), saved.data_ptr(), saved_bytes, dxb.data_ptr(),
+                             dwb.data_ptr(), M, N, K, wsb.data_ptr(), ws_b, stream))
+    y_ref, saved_ref = fp8.fp8_linear_fwd_save(x, w)
+    dx_ref, dw_ref = fp8.fp8_linear_bwd(dy, saved_ref, K)
+    torch.cuda.synchronize()
+    for buf, n, name in ((saved, saved_bytes, "saved"), (wsf, ws_f, "fwd workspace"),
+                         (wsb, ws_b, "bwd workspace"), (yb, 2 * M * N, "y"),
+                         (dxb, 2 * M * K, "dx"), (dwb, 2 * N * K, "dw")):
+        assert bool((buf[n:] == canary).all()), f"{name}: bytes past its size were written"
+    for buf, ref, name in ((yb, y_ref, "y"), (dxb, dx_ref, "dx"), (dwb, dw_ref, "dw")):
+        got = buf[: ref.numel() * 2].view(torch.int16).view(ref.shape)
+        assert torch.equal(got, ref.view(torch.int16)), f"{name} differs from the binding's"
