@@ -204,6 +204,39 @@ def test_quant_outputs_stay_in_bounds_and_honour_strides(gpu):
     assert_f32_equal(host_f32(rt), orc, "canary T recip")
 
 
+@pytest.mark.parametrize("block", ["1x128", "128x128"])
+def test_quant_dual_outputs_stay_in_bounds(gpu, block):
+    """Both layouts of the dual quantizer written into canary-padded code
+    buffers (ld > width) and strided views of NaN-filled scale buffers, from
+    a 208 x 384 input (a partly filled last row block): bit-exact against
+    the oracle, and nothing outside the logical regions changes."""
+    rows, cols = 208, 384
+    x = inputs.randn_bf16((rows, cols), seed=inputs.tensor_seed(14, "x"))
+    xd = x.to(gpu)
+    ni, nj = fp8.ops.scale_grid(rows, cols, block, False)
+    ti, tj = fp8.ops.scale_grid(rows, cols, block, True)
+    qbuf = torch.full((rows, cols + 32), 0xA5, dtype=torch.uint8, device=gpu)
+    qtbuf = torch.full((cols, rows + 48), 0x5A, dtype=torch.uint8, device=gpu)
+    rbuf = torch.full((ni, nj + 2), float("nan"), dtype=torch.float32, device=gpu)
+    rtbuf = torch.full((ti, tj + 3), float("nan"), dtype=torch.float32, device=gpu)
+    say("quant dual canary", block)
+    fp8.fp8_blockwise_quant_dual(xd, block, q=qbuf[:, :cols], recip=rbuf[:, :nj],
+                                 qt=qtbuf[:, :rows], recip_t=rtbuf[:, :tj])
+    torch.cuda.synchronize()
+    if block == "1x128":
+        oq, orc = quant.quant_1x128(bits(x))
+        oqt, ort = quant.quant_1x128_along_rows(bits(x))
+    else:
+        oq, orc = quant.quant_128x128(bits(x))
+        oqt, ort = quant.quant_128x128_transposed(bits(x))
+    assert_codes_equal(host_u8(qbuf[:, :cols]), oq, f"dual canary {block} codes")
+    assert_codes_equal(host_u8(qtbuf[:, :rows]), oqt, f"dual canary {block} codes^T")
+    assert_f32_equal(host_f32(rbuf[:, :nj]), orc, f"dual canary {block} recip")
+    assert_f32_equal(host_f32(rtbuf[:, :tj]), ort, f"dual canary {block} recip^T")
+    assert np.all(host_u8(qbuf[:, cols:]) == 0xA5) and np.all(host_u8(qtbuf[:, rows:]) == 0x5A)
+    assert np.all(np.isnan(host_f32(rbuf[:, nj:]))) and np.all(np.isnan(host_f32(rtbuf[:, tj:])))
+
+
 def test_quant_deterministic(gpu):
     x = inputs.randn_bf16((512, 1024), seed=10).to(gpu)
     say("quant determinism")
