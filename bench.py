@@ -182,22 +182,44 @@ def run_gpu(steps, warmup, seed, plan_fn=None, wl=None, shape=(M, N, K)):
             "quant_gbps": qbytes / (qms * 1e-3) / 1e9, "quant_us": qms * 1e3, "workload": wl}
 
 
-def _time_quant(xs, qs, recips, block, reps):
+def _time_quant(xs, qs, recips, block, reps, graph=False):
     """Average duration (ms) of one quantizer call, cycling through the
     buffers so consecutive calls touch different memory; one HIP event pair
-    around the whole sequence on the launch stream."""
+    around the whole sequence on the launch stream.  With `graph` the
+    sequence is captured once as a HIP graph and replayed, so the host's
+    per-call cost (Python, argument checks) drops out of the figure."""
     import blockwise_scaled_fp8_amd as fp8
     n = len(xs)
     for i in range(min(n, 3)):
         fp8.fp8_blockwise_quant(xs[i], block, q=qs[i], recip=recips[i])
     torch.cuda.synchronize()
     calls = max(reps, 2 * n)
+
+    def seq():
+        for i in range(calls):
+            fp8.fp8_blockwise_quant(xs[i % n], block, q=qs[i % n], recip=recips[i % n])
+
+    g = None
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            seq()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            seq()
+        g.replay()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(calls):
-        fp8.fp8_blockwise_quant(xs[i % n], block, q=qs[i % n], recip=recips[i % n])
+    if g is not None:
+        g.replay()
+    else:
+        seq()
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / calls
@@ -210,7 +232,9 @@ def quant_standalone(seed, sizes=(1024, 2048, 4096, 8192, 16384, 32768), reps=10
     inputs total at least 1 GiB, four times the 256 MB Infinity Cache, so
     every call streams from HBM (32768^2 is one 2 GiB input).  Algorithmic bytes as
     in the step (2 B read + 1 B written per element + 4 B per scale).  The
-    headline entries are the 32768^2 ones; small sizes are launch-bound."""
+    headline entries are the 32768^2 ones; below 8192^2 the calls are
+    launch-bound, and those sizes are also timed replayed from a HIP graph
+    (graph_avg_us), which leaves out the host's per-call cost."""
     from synth import inputs
     dev = torch.device("cuda", 0)
     sweep = {}
@@ -228,6 +252,11 @@ def quant_standalone(seed, sizes=(1024, 2048, 4096, 8192, 16384, 32768), reps=10
             gbps = quant_bytes(size, size, block) / (ms * 1e-3) / 1e9
             entry[block] = {"avg_us": round(ms * 1e3, 2), "gbps": round(gbps, 1),
                             "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)}
+            if size < 8192:
+                # launch-bound sizes: the same calls replayed from a HIP graph
+                gms = _time_quant(xs, qs, recips, block, reps, graph=True)
+                entry[block]["graph_avg_us"] = round(gms * 1e3, 2)
+                entry[block]["graph_gbps"] = round(quant_bytes(size, size, block) / (gms * 1e-3) / 1e9, 1)
             del recips
         sweep[str(size)] = entry
         del xs, qs, x0
