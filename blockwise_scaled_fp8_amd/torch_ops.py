@@ -210,6 +210,12 @@ class Float8BlockwiseLinear(torch.nn.Module):
         if torch.is_grad_enabled() and (x.requires_grad or self.weight.requires_grad):
             # Training: quantize X and W once into both layouts and keep the
             # transposed fp8 codes (half the bytes of the bf16 X) for backward.
+            # The weight gradient contracts over the tokens in 1x128 blocks,
+            # so their count must be a multiple of 128; say so here rather
+            # than in the backward.
+            if x2.shape[0] % 128:
+                raise ValueError(f"training needs the token count ({x2.shape[0]}) to be a multiple "
+                                 "of 128: the weight gradient contracts over tokens in blocks of 128")
             y = _FusedQuantLinear.apply(x2, self.weight)
         else:
             y = torch.ops.fp8bw.linear_fwd(x2, self.weight)

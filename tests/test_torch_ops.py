@@ -76,3 +76,15 @@ def test_cpu_tensors_are_refused():
     m = fp8.Float8BlockwiseLinear(128, 128)
     with pytest.raises(ValueError, match="CUDA"):
         m(torch.zeros(128, 128, dtype=torch.bfloat16))
+
+
+def test_training_token_count_checked_in_forward():
+    """The weight gradient contracts over tokens in 1x128 blocks: a training
+    forward with a token count that is not a multiple of 128 is refused at
+    once, while inference (no gradient) takes any count."""
+    m = fp8.Float8BlockwiseLinear(256, 128, device="meta")
+    with pytest.raises(ValueError, match="multiple of 128"):
+        m(_meta(2, 50, 256, grad=True))
+    with torch.no_grad():
+        y = m(_meta(2, 50, 256, grad=False))
+    assert y.shape == (2, 50, 128)
