@@ -375,14 +375,18 @@ __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* 
   if constexpr (MODE != kTensorwise) {
     const __amdgpu_buffer_rsrc_t rars =
         buffer_rsrc(p.ra + (int64_t)kb * p.ra_s_kb + m0, (int64_t)(p.M - m0) * 4);
-    // ra lands transposed per wave row band of 16 TMV rows: LDS slot
-    // k = 16 TMV h + TMV r + i holds row 16 TMV h + 16 i + r, so that a lane
-    // (fragment row r) finds the scales of its TMV sub-tiles side by side.
+    // ra lands transposed per wave row band of 16 TMV rows, in groups of
+    // four sub-tiles: LDS slot k = 16 TMV h + 64 q + 4 r + v holds row
+    // 16 TMV h + 16 (4 q + v) + r, so a lane (fragment row r) finds the
+    // scales of sub-tiles 4q .. 4q + 3 in one 16-byte chunk, and the 16 rows'
+    // chunks of one group are 256 consecutive bytes (one conflict-free pass).
 #pragma unroll
     for (int i = 0; i < RAI; ++i) {
       const int blk = (wave + NW * i) % RAB;
       const int k = 64 * blk + lane;
-      const int row = (k / (16 * TMV)) * (16 * TMV) + 16 * (k % TMV) + (k % (16 * TMV)) / TMV;
+      static_assert(TMV % 4 == 0, "scales grouped by four sub-tiles");
+      const int kb16 = k % (16 * TMV);
+      const int row = (k / (16 * TMV)) * (16 * TMV) + 16 * (4 * (kb16 / 64) + kb16 % 4) + (kb16 % 64) / 4;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rars, (lds_void_t*)(sra + 64 * blk), 4, row * 4,
                                                0, 0, 0);
     }
@@ -615,7 +619,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     uint32_t a_hi = (wm0 + frow) * 128 + (((2 * fhalf + 1) ^ swz(wm0 + frow)) << 4);
     uint32_t b_lo = (wn0 + frow) * 128 + (((2 * fhalf) ^ swz(wn0 + frow)) << 4);
     uint32_t b_hi = (wn0 + frow) * 128 + (((2 * fhalf + 1) ^ swz(wn0 + frow)) << 4);
-    uint32_t ra_off = (wm0 + TM * frow) * 4;
+    uint32_t ra_off = (wm0 + 4 * frow) * 4;
     uint32_t rb_off = (wn0 + 4 * fhalf) * 4;
     asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(ra_off), "+v"(rb_off));
     const uint8_t* tA = sA[st];
@@ -635,7 +639,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     if constexpr (SCALED) {
 #pragma unroll
       for (int q = 0; q < TM / 4; ++q) {
-        const v4f s4 = *(const v4f*)(tRa + ra_off + 16 * q);
+        const v4f s4 = *(const v4f*)(tRa + ra_off + 256 * q);
 #pragma unroll
         for (int v = 0; v < 4; ++v) sa[4 * q + v] = s4[v];
       }
