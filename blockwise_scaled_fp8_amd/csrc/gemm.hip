@@ -627,9 +627,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     const uint8_t* tRa = (const uint8_t*)sRa[st];
     const uint8_t* tRb = (const uint8_t*)sRb[st];
 
+    constexpr int PF = kRowPrefetch < TM ? kRowPrefetch : TM - 1;
+    constexpr int NS = PF + 1;
     v8i bf[TN];
+    v8i af[NS];
+    if constexpr (MODE == kTensorwise) {
+      // Fragment reads in the order the first MFMAs use them (B column 0,
+      // A row 0, the other B columns, the prefetched A rows): LDS reads
+      // complete in order, so the first MFMA waits for two fragments, not
+      // for all of the K block's head (tensorwise +2%; with block scales,
+      // whose products the head also computes, it measured slower).
+      bf[0] = load_frag_at(tB, b_lo, b_hi);
+      af[0] = load_frag_at(tA, a_lo, a_hi);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bf[j] = load_frag_at(tB, b_lo + 2048 * j, b_hi + 2048 * j);
+      for (int j = 1; j < TN; ++j) bf[j] = load_frag_at(tB, b_lo + 2048 * j, b_hi + 2048 * j);
+#pragma unroll
+      for (int i = 1; i < PF; ++i) af[i] = load_frag_at(tA, a_lo + 2048 * i, a_hi + 2048 * i);
+      __builtin_amdgcn_sched_barrier(0);   // keep that order
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[j] = load_frag_at(tB, b_lo + 2048 * j, b_hi + 2048 * j);
+    }
     // Row scales of this lane's TM sub-tile rows (one row per sub-tile:
     // the partials are computed transposed, see below), times the 128x128
     // B scale of the wave's columns; per-row B scales of the lane's four
@@ -663,11 +681,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     // A rows are read PF rows ahead into a ring of PF + 1 fragment slots:
     // row i + PF goes into the slot of row i - 1 as soon as row i starts
     // (row i - 1's MFMAs are issued).
-    constexpr int PF = kRowPrefetch < TM ? kRowPrefetch : TM - 1;
-    constexpr int NS = PF + 1;
-    v8i af[NS];
+    if constexpr (MODE != kTensorwise) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) af[i] = load_frag_at(tA, a_lo + 2048 * i, a_hi + 2048 * i);
+      for (int i = 0; i < PF; ++i) af[i] = load_frag_at(tA, a_lo + 2048 * i, a_hi + 2048 * i);
+    }
     v4f ring[kRingDelay + 1];
 #pragma unroll
     for (int t = 0; t < T + kRingDelay; ++t) {
