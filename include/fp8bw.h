@@ -216,6 +216,16 @@ int fp8_scaled_gemm_tensorwise(const void* a, int64_t lda, const float* ra, cons
  *   Every other argument, status and workspace rule is that of the call
  *   without _bias.
  */
+int fp8_scaled_gemm_blockwise_bias(const void* a, int64_t lda, const float* ra, int64_t ra_s_row,
+                                   int64_t ra_s_kb, const void* b, int64_t ldb, const float* rb,
+                                   int64_t rb_s_row, int64_t rb_s_kb, int b_block, int64_t M,
+                                   int64_t N, int64_t K, const void* bias, void* out, int64_t ldo,
+                                   int out_dtype, void* ws, size_t ws_bytes, void* stream);
+int fp8_scaled_gemm_tensorwise_bias(const void* a, int64_t lda, const float* ra, const void* b,
+                                    int64_t ldb, const float* rb, int64_t M, int64_t N, int64_t K,
+                                    const void* bias, void* out, int64_t ldo, int out_dtype,
+                                    void* stream);
+
 /*
  * fp8_scaled_grouped_gemm_blockwise -- one launch for G GEMMs that share N
  * and K and split the rows of A and out into consecutive groups, each with
@@ -248,16 +258,6 @@ int fp8_scaled_grouped_gemm_blockwise(const void* a, int64_t lda, const float* r
                                       int64_t rb_s_kb, int64_t rb_s_group, int groups,
                                       const int* group_end, int64_t M, int64_t N, int64_t K,
                                       void* out, int64_t ldo, int out_dtype, void* stream);
-
-int fp8_scaled_gemm_blockwise_bias(const void* a, int64_t lda, const float* ra, int64_t ra_s_row,
-                                   int64_t ra_s_kb, const void* b, int64_t ldb, const float* rb,
-                                   int64_t rb_s_row, int64_t rb_s_kb, int b_block, int64_t M,
-                                   int64_t N, int64_t K, const void* bias, void* out, int64_t ldo,
-                                   int out_dtype, void* ws, size_t ws_bytes, void* stream);
-int fp8_scaled_gemm_tensorwise_bias(const void* a, int64_t lda, const float* ra, const void* b,
-                                    int64_t ldb, const float* rb, int64_t M, int64_t N, int64_t K,
-                                    const void* bias, void* out, int64_t ldo, int out_dtype,
-                                    void* stream);
 
 /*
  * FP8 blockwise linear layer, fwd / dgrad / wgrad ([INTEG] Summary:
