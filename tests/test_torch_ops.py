@@ -69,7 +69,7 @@ def test_module_interface():
     m = fp8.Float8BlockwiseLinear.from_linear(lin)
     assert torch.equal(m.weight, lin.weight.detach().to(torch.bfloat16))
     bound = 1 / 256 ** 0.5
-    assert float(fp8.Float8BlockwiseLinear(256, 128).weight.abs().max()) <= bound
+    assert float(fp8.Float8BlockwiseLinear(256, 128).weight.detach().abs().max()) <= bound
 
 
 def test_cpu_tensors_are_refused():
