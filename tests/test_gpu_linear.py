@@ -178,3 +178,20 @@ def test_fused_linear_canaries(gpu):
     for buf, ref, name in ((yb, y_ref, "y"), (dxb, dx_ref, "dx"), (dwb, dw_ref, "dw")):
         got = buf[: ref.numel() * 2].view(torch.int16).view(ref.shape)
         assert torch.equal(got, ref.view(torch.int16)), f"{name} differs from the binding's"
+
+
+@pytest.mark.parametrize("mnk", [(208, 256, 384), (16, 128, 128)])
+def test_fused_forward_ragged_tokens(gpu, mnk):
+    """fp8_linear_fwd_save takes a token count that is not a multiple of 128
+    (its saved X^T codes end in a partial 1x128 block along M): Y equals
+    fp8_linear_fwd's bit for bit, and the backward, whose weight gradient
+    contracts over tokens in 128-blocks, refuses the shape before launching."""
+    M, N, K = mnk
+    x, w, dy = (t.to(gpu) for t in _inputs(M, N, K, seed=11, device="cpu"))
+    say("fused forward ragged", mnk)
+    y, saved = fp8.fp8_linear_fwd_save(x, w)
+    y_ref = fp8.fp8_linear_fwd(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    with pytest.raises(fp8.FP8BWError, match="multiples of 128"):
+        fp8.fp8_linear_bwd(dy, saved, K)
