@@ -83,3 +83,17 @@ def test_grouped_moe_like_sampled(gpu):
 def test_grouped_malformed_table_is_clamped(gpu):
     """Decreasing ends and ends past M are clamped to [previous end, M]."""
     _case(gpu, 4, 512, 256, 256, [200, 100, 9999, 50], "f32", seed=54)
+
+
+def test_grouped_benchmark_configuration_sampled(gpu):
+    """The configuration the benchmark times: the 16640 tokens of the
+    forward shape split over 8 experts with the same seeded multinomial
+    sizes, N 5120, K 8192, bf16 out; sampled rows (every group's first and
+    last row, and random ones) against the oracle."""
+    G, M, N, K = 8, 16640, 5120, 8192
+    sizes = np.random.default_rng(0).multinomial(M, np.ones(G) / G)
+    ends = np.cumsum(sizes)
+    rng = np.random.default_rng(55)
+    starts = np.r_[0, ends[:-1]]
+    sample = np.unique(np.r_[starts, ends - 1, rng.integers(0, M, 16)])
+    _case(gpu, G, M, N, K, ends, "bf16", seed=55, sample=sample)
