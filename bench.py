@@ -382,17 +382,17 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quant-standalone", action="store_true",
-                    help="skip the standalone 32768^2 quantizer timing")
+                    help="skip the standalone quantizer sweep (S x S, S = 1024 .. 32768)")
     ap.add_argument("--step-only", action="store_true",
-                    help="time the step alone: no fused-quantization step, grouped GEMM or "
-                         "standalone quantizers (for profiling runs)")
+                    help="time the step alone: no separate-quantizer step, second linear shape, "
+                         "grouped GEMM or standalone quantizers (for profiling runs)")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build runs "
-              "the hot path on a single MI355X; multi-GPU sharding is a design note, not a "
-              "measured configuration.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the hot path runs "
+              "on a single MI355X; sharding it across GPUs is described, not measured.",
+              file=sys.stderr)
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs as a single process on one GPU", file=sys.stderr)
