@@ -3,8 +3,9 @@
 Captured into one graph: the fused training step (fp8_linear_fwd_save +
 fp8_linear_bwd: three dual quantizers and three GEMMs), the per-tensor path
 (two-kernel quantizer, tensorwise GEMM), a whole-problem split-K GEMM
-(partials + ordered reduce) and a 272-tile GEMM (full rounds of 256x256 tiles,
-then the leftover tiles split over K and reduced).  No library call records a
+(partials + ordered reduce), a 272-tile GEMM (full rounds of 256x256 tiles,
+then the leftover tiles split over K and reduced) and a grouped GEMM whose
+group boundaries are read on the device.  No library call records a
 memset or reads a device value on the host, and every kernel is
 deterministic, so each replay must reproduce the eager outputs bit for bit.
 The graph is replayed several times with eager work and synchronizations in
@@ -26,7 +27,7 @@ def _bits(t):
         t.view(torch.int32) if t.dtype == torch.float32 else t)
 
 
-def _step(x, w, dy, a, ra, b, rb, a2, ra2, b2, rb2):
+def _step(x, w, dy, a, ra, b, rb, a2, ra2, b2, rb2, wg, rwg, ends):
     y, saved = fp8.fp8_linear_fwd_save(x, w)
     dx, dw = fp8.fp8_linear_bwd(dy, saved, x.shape[1])
     xq, xr = fp8.fp8_tensorwise_quant(x)
@@ -34,7 +35,8 @@ def _step(x, w, dy, a, ra, b, rb, a2, ra2, b2, rb2):
     yt = fp8.fp8_scaled_gemm_tensorwise(xq, xr, wq, wr)
     ys = fp8.fp8_scaled_gemm_blockwise(a, ra, b, rb, "128x128", out_dtype=torch.float32)
     yr = fp8.fp8_scaled_gemm_blockwise(a2, ra2, b2, rb2, "128x128")
-    return [y, saved, dx, dw, xq, xr, yt, ys, yr]
+    yg = fp8.fp8_scaled_grouped_gemm_blockwise(a2, ra2, wg, rwg, ends)
+    return [y, saved, dx, dw, xq, xr, yt, ys, yr, yg]
 
 
 def test_graph_replays_match_eager(gpu):
@@ -53,7 +55,11 @@ def test_graph_replays_match_eager(gpu):
         inputs.randn_bf16((4352, 2048), seed=inputs.tensor_seed(72, "a"), device=gpu), "1x128")
     b2, rb2 = fp8.fp8_blockwise_quant(
         inputs.randn_bf16((4096, 2048), seed=inputs.tensor_seed(72, "b"), device=gpu), "128x128")
-    ops = (x, w, dy, a, ra, b, rb, a2, ra2, b2, rb2)
+    # three experts over a2's 4352 rows, reading their boundaries on the device
+    wg = torch.stack([b2[:512], b2[512:1024], b2[1024:1536]])
+    rwg = torch.stack([rb2[:4], rb2[4:8], rb2[8:12]])
+    ends = torch.tensor([1000, 2900, 4352], dtype=torch.int32, device=gpu)
+    ops = (x, w, dy, a, ra, b, rb, a2, ra2, b2, rb2, wg, rwg, ends)
 
     say("graph: eager step")
     eager = [t.clone() for t in _step(*ops)]
