@@ -29,9 +29,11 @@ def rel_frobenius(ref, out):
 
 
 def bf16_ulp(x):
-    """Spacing of bf16 numbers at |x| (float64): 2^(floor(log2|x|) - 7);
-    below the normal range, the subnormal spacing 2^-133."""
+    """Spacing of bf16 numbers at |x| (float64): the gap from |x| to the next
+    larger bf16 value, 2^(floor(log2|x|) - 7) for normal |x| >= 2^-126; zero
+    and subnormal |x| get the subnormal spacing 2^-133.  (bf16 keeps 8
+    significant bits, 7 stored, and the fp32 exponent range.)"""
     a = np.abs(np.asarray(x, dtype=np.float64))
-    _, ex = np.frexp(a)
-    e = np.maximum(ex.astype(np.int64) - 1, -126)
+    _, ex = np.frexp(a)                      # a = f 2^ex with f in [0.5, 1)
+    e = np.where(a >= 2.0 ** -126, ex.astype(np.int64) - 1, -126)
     return np.ldexp(1.0, e - 7)
