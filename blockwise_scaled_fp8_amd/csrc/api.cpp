@@ -223,15 +223,13 @@ static int gemm_blockwise_impl(const void* a, int64_t lda, const float* ra, int6
   if (kb > 0) {
     if (!ra || !rb) return fail(FP8BW_ERR_NULL, "ra and rb must be non-null");
     if (!aligned(ra, 4) || !aligned(rb, 4)) return fail(FP8BW_ERR_ALIGN, "ra/rb must be 4-byte aligned");
-    // Strides of size-1 dimensions are never used and may be anything.
-    if ((M > 1 && ra_s_row != 1) || (kb > 1 && ra_s_kb < M))
-      return fail(FP8BW_ERR_LAYOUT, "ra must be column-major: ra_s_row == 1 and ra_s_kb >= M");
-    if (b_block == FP8BW_BLOCK_1x128) {
-      if ((N > 1 && rb_s_row != 1) || (kb > 1 && rb_s_kb < N))
-        return fail(FP8BW_ERR_LAYOUT, "1x128 rb must be column-major: rb_s_row == 1 and rb_s_kb >= N");
-    } else if (!strides_injective(cdiv(N, 128), kb, rb_s_row, rb_s_kb)) {
+    // Any non-overlapping strides (column-major, row-major, views with
+    // padding); strides of size-1 dimensions are never used.
+    if (!strides_injective(M, kb, ra_s_row, ra_s_kb))
+      return fail(FP8BW_ERR_LAYOUT, "ra strides (%lld, %lld) alias or are negative", (long long)ra_s_row, (long long)ra_s_kb);
+    const int64_t nrb = b_block == FP8BW_BLOCK_1x128 ? N : cdiv(N, 128);
+    if (!strides_injective(nrb, kb, rb_s_row, rb_s_kb))
       return fail(FP8BW_ERR_LAYOUT, "rb strides (%lld, %lld) alias or are negative", (long long)rb_s_row, (long long)rb_s_kb);
-    }
   }
   fp8bw::GemmProblem p;
   p.a = a; p.lda = lda; p.b = b; p.ldb = ldb;
@@ -357,7 +355,7 @@ FP8BW_API int fp8_scaled_grouped_gemm_blockwise(
   p.mode = fp8bw::kBlockB128;
   p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
   if (!fp8bw::grouped_gemm_ok(p, groups))
-    return fail(FP8BW_ERR_UNSUPPORTED, "grouped GEMM needs N >= 128 and 32-bit operand offsets");
+    return fail(FP8BW_ERR_UNSUPPORTED, "grouped GEMM problem not supported");
   return hip_status(fp8bw::launch_grouped_gemm(p, groups, group_end, b_s_group, rb_s_group,
                                                (hipStream_t)stream),
                     "fp8_scaled_grouped_gemm_blockwise");

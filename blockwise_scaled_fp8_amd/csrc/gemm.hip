@@ -43,8 +43,8 @@ struct GemmArgs {
   void* out;
   float* partial;
   int64_t lda, ldb, ldo;
-  int64_t ra_s_kb;   // ra row stride is 1 (column-major scales)
-  int64_t rb_s_row, rb_s_kb;
+  int64_t ra_s_row, ra_s_kb;   // ra[m * ra_s_row + kb * ra_s_kb]
+  int64_t rb_s_row, rb_s_kb;   // rb[beta(n) * rb_s_row + kb * rb_s_kb]
   int M, N, K;
   int kblocks;
   int tiles_m, tiles_n;
@@ -118,8 +118,11 @@ __device__ __forceinline__ v8i load_frag_at(const uint8_t* tile, uint32_t lo, ui
   return f;
 }
 
+template <int BM, int OUT>
+__device__ __forceinline__ bool locate_group_tile(GemmArgs& p, int t, int* tm, int* tn, int* row0);
+
 template <int BM, int BN, int MODE, int OUT, bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
+__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p_in) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int ACH = BM / 32, BCH = BN / 32;   // 16-byte chunks per thread per K block
@@ -134,8 +137,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-  const int tile = blockIdx.x;
-  const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+  GemmArgs p = p_in;
+  int tm, tn;
+  if (p.groups > 0) {
+    // Grouped GEMM: p now addresses this tile's group (rows clamp to it).
+    int row0;
+    if (!locate_group_tile<BM, OUT>(p, blockIdx.x, &tm, &tn, &row0)) return;
+  } else {
+    tm = blockIdx.x / p.tiles_n;
+    tn = blockIdx.x - tm * p.tiles_n;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int kb_begin = blockIdx.y * p.kb_per_split;
   const int kb_end = min(p.kblocks, kb_begin + p.kb_per_split);
@@ -172,14 +183,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
       if (kok) rB[i] = *(const uint4*)(pb[i] + koff);
     }
     if (MODE != kTensorwise) {
-      if (tid < BM) rsa = p.ra[(int64_t)kb * p.ra_s_kb + min(m0 + tid, p.M - 1)];
+      if (tid < BM) rsa = p.ra[(int64_t)kb * p.ra_s_kb + (int64_t)min(m0 + tid, p.M - 1) * p.ra_s_row];
       if (MODE == kBlockB128) {
         if (tid < SB) {
           const int nb = min(n0 / 128 + tid, (p.N - 1) / 128);
           rsb = p.rb[(int64_t)nb * p.rb_s_row + (int64_t)kb * p.rb_s_kb];
         }
       } else {
-        if (tid < SB) rsb = p.rb[min(n0 + tid, p.N - 1) + (int64_t)kb * p.rb_s_kb];
+        if (tid < SB) rsb = p.rb[(int64_t)min(n0 + tid, p.N - 1) * p.rb_s_row + (int64_t)kb * p.rb_s_kb];
       }
     }
   };
@@ -344,24 +355,31 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 }
 
 // Raw buffer descriptor over `bytes` bytes from `base` (stride 0; gfx9
-// dword3: 32-bit data format, no swizzle).  The hardware range check makes
-// any access at or past `bytes` read as zero, which is how ragged row tiles
-// get their missing rows.
+// dword3: 32-bit data format, no swizzle).  The large-tile kernels never
+// rely on its range check: every direct load they issue addresses a row
+// that exists (ragged edge tiles move their operand window back inside the
+// matrix, see gemm_v2_kernel), because the check covers only the per-lane
+// vector offset and not the scalar offset the row octets and K blocks use.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
   const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
 // One stage of direct buffer->LDS loads for K block kb (see gemm_v2_kernel).
-// ars / brs cover the tile's rows of A / B from its first row on; a_voff /
-// b_voff are this lane's byte offsets in its wave's first row octet, and
-// octet i is 8 NW rows further (soffset), K block kb 128 bytes further.
-template <int AI, int BI, int RAI, int RBI, int RAB, int RBB, int NW, int MODE, int TMV>
+// ars / brs cover the tile's BM rows of A / BN rows of B; a_voff / b_voff
+// are this lane's byte offsets in its wave's first row octet, and octet i is
+// 8 NW rows further (soffset), K block kb 128 bytes further.  ra_voff /
+// rb_voff are this lane's byte offsets of its scale slots (row times the
+// scale row stride), precomputed by the caller; ra_base / rb_base point at
+// the scales of the tile's first row (row block) in K block 0.
+template <int AI, int BI, int RAI, int RBI, int RAB, int RBB, int NW, int MODE>
 __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* sa, uint8_t* sb,
                                             float* sra, float* srb, __amdgpu_buffer_rsrc_t ars,
                                             __amdgpu_buffer_rsrc_t brs, uint32_t a_voff,
-                                            uint32_t b_voff, uint32_t rbn_voff, int wave, int lane,
-                                            int m0, int n0) {
+                                            uint32_t b_voff, const uint32_t (&ra_voff)[RAI > 0 ? RAI : 1],
+                                            const uint32_t (&rb_voff)[RBI > 0 ? RBI : 1],
+                                            const float* ra_base, int64_t ra_bytes,
+                                            const float* rb_base, int64_t rb_bytes, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel stub
   const int ko = kb * 128;
 #pragma unroll
@@ -373,38 +391,19 @@ __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void_t*)(sb + (wave + NW * i) * 1024), 16,
                                              b_voff, ko + 8 * NW * i * (int)p.ldb, 0, 0);
   if constexpr (MODE != kTensorwise) {
-    const __amdgpu_buffer_rsrc_t rars =
-        buffer_rsrc(p.ra + (int64_t)kb * p.ra_s_kb + m0, (int64_t)(p.M - m0) * 4);
-    // ra lands transposed per wave row band of 16 TMV rows, in groups of
-    // four sub-tiles: LDS slot k = 16 TMV h + 64 q + 4 r + v holds row
-    // 16 TMV h + 16 (4 q + v) + r, so a lane (fragment row r) finds the
-    // scales of sub-tiles 4q .. 4q + 3 in one 16-byte chunk, and the 16 rows'
-    // chunks of one group are 256 consecutive bytes (one conflict-free pass).
+    const __amdgpu_buffer_rsrc_t rars = buffer_rsrc(ra_base + (int64_t)kb * p.ra_s_kb, ra_bytes);
 #pragma unroll
     for (int i = 0; i < RAI; ++i) {
       const int blk = (wave + NW * i) % RAB;
-      const int k = 64 * blk + lane;
-      static_assert(TMV % 4 == 0, "scales grouped by four sub-tiles");
-      const int kb16 = k % (16 * TMV);
-      const int row = (k / (16 * TMV)) * (16 * TMV) + 16 * (4 * (kb16 / 64) + kb16 % 4) + (kb16 % 64) / 4;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rars, (lds_void_t*)(sra + 64 * blk), 4, row * 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rars, (lds_void_t*)(sra + 64 * blk), 4, ra_voff[i],
                                                0, 0, 0);
     }
-    if constexpr (MODE == kBlockB128) {
-      const __amdgpu_buffer_rsrc_t rbrs = buffer_rsrc(
-          p.rb + (int64_t)kb * p.rb_s_kb, ((int64_t)((p.N - 1) / 128) * p.rb_s_row + 1) * 4);
+    const __amdgpu_buffer_rsrc_t rbrs = buffer_rsrc(rb_base + (int64_t)kb * p.rb_s_kb, rb_bytes);
 #pragma unroll
-      for (int i = 0; i < RBI; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbrs, (lds_void_t*)srb, 4, rbn_voff, 0, 0, 0);
-    } else {
-      const __amdgpu_buffer_rsrc_t rbrs =
-          buffer_rsrc(p.rb + (int64_t)kb * p.rb_s_kb + n0, (int64_t)(p.N - n0) * 4);
-#pragma unroll
-      for (int i = 0; i < RBI; ++i) {
-        const int blk = (wave + NW * i) % RBB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbrs, (lds_void_t*)(srb + 64 * blk), 4, lane * 4,
-                                                 256 * blk, 0, 0);
-      }
+    for (int i = 0; i < RBI; ++i) {
+      const int blk = MODE == kBlockB128 ? 0 : (wave + NW * i) % RBB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbrs, (lds_void_t*)(srb + 64 * blk), 4, rb_voff[i],
+                                               0, 0, 0);
     }
   }
 #endif
@@ -414,10 +413,14 @@ __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* 
 // sub-tile (i, j), row mb + 16 i + frow and the four columns
 // nb + 16 j + 4 fhalf + v.  The four are stored with one 8-byte (bf16) or
 // 16-byte (fp32) store when the output rows allow it, else one by one.
+// GUARD: only rows in [m_lo, M) and columns in [n_lo, N) are stored (an
+// edge tile computes rows and columns of its neighbour, see gemm_v2_kernel);
+// a quad is stored with one vector store only if it lies wholly inside and
+// starts on a 4-column boundary.
 template <bool GUARD, int TM, int TN, int MODE, int OUT, bool SPLIT>
 __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM][TN], float tscale,
-                                          int mb, int nb, int frow, int fhalf, float* pbase,
-                                          int64_t pld, int pm0, int pn0) {
+                                          int mb, int nb, int m_lo, int n_lo, int frow, int fhalf,
+                                          float* pbase, int64_t pld, int pm0, int pn0) {
   const bool vec = SPLIT ? ((pld & 3) == 0 && ((size_t)pbase & 15) == 0)
                          : ((p.ldo & 3) == 0 && ((size_t)p.out & 15) == 0);
 #pragma unroll
@@ -435,7 +438,8 @@ __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM
           if (!GUARD || nq + v < p.N) val[v] += bias_at(p.bias, nq + v);
         }
       }
-      if (vec && (!GUARD || (m < p.M && nq + 3 < p.N))) {
+      if (vec && (!GUARD || (m >= m_lo && m < p.M && nq >= n_lo && nq + 3 < p.N &&
+                             (nq & 3) == 0))) {
         if constexpr (SPLIT) {
           *(float4*)(pbase + (int64_t)(m - pm0) * pld + (nq - pn0)) =
               make_float4(val[0], val[1], val[2], val[3]);
@@ -452,7 +456,7 @@ __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int n = nq + v;
-          if (!GUARD || (m < p.M && n < p.N)) {
+          if (!GUARD || (m >= m_lo && m < p.M && n >= n_lo && n < p.N)) {
             if constexpr (SPLIT) {
               pbase[(int64_t)(m - pm0) * pld + (n - pn0)] = val[v];
             } else if constexpr (OUT == kOutBf16) {
@@ -473,7 +477,7 @@ __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM
 // inside a group).  Returns false for ids past the last tile (the grid is
 // sized for the worst case of every group's last row tile being partial).
 template <int BM, int OUT>
-__device__ __forceinline__ bool locate_group_tile(GemmArgs& p, int t, int* tm, int* tn) {
+__device__ __forceinline__ bool locate_group_tile(GemmArgs& p, int t, int* tm, int* tn, int* row0_out) {
   int start = 0, row0 = 0;
   for (int g = 0; g < p.groups; ++g) {
     const int end = max(row0, min(p.group_end[g], p.M));
@@ -482,8 +486,9 @@ __device__ __forceinline__ bool locate_group_tile(GemmArgs& p, int t, int* tm, i
     const int nt = mt * p.tiles_n;
     if (t < start + nt) {
       tile_to_mn(t - start, mt, p.tiles_n, tm, tn);
+      *row0_out = row0;
       p.a += (int64_t)row0 * p.lda;
-      p.ra += row0;
+      p.ra += (int64_t)row0 * p.ra_s_row;
       p.out = (uint8_t*)p.out + (int64_t)row0 * p.ldo * (OUT == kOutBf16 ? 2 : 4);
       p.b += (int64_t)g * p.b_s_group;
       p.rb += (int64_t)g * p.rb_s_group;
@@ -546,12 +551,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   int tm, tn;
   GemmArgs p = p_in;
   const int tile_local = xcd_remap(blockIdx.x, gridDim.x);
+  // Output tile [m0, m0 + BM) x [n0, n0 + BN).  The operand window the tile
+  // loads, [ml, ml + BM) x [nl, nl + BN), is the same except at a ragged
+  // edge, where it moves back to end exactly at the last row of A (of B):
+  // every direct load then reads an existing row, and the edge tile stores
+  // only its own rows and columns.  The host guarantees M >= BM and
+  // N >= BN (the whole A of a grouped GEMM has at least BM rows) and, for
+  // 128x128 B scales, N % 64 == 0, so nl stays a multiple of 64 and a
+  // wave's 64 columns keep a single B scale block.
+  int ml;
   if (p.groups > 0) {
-    if (!locate_group_tile<BM, OUT>(p, tile_local, &tm, &tn)) return;
+    int row0;
+    if (!locate_group_tile<BM, OUT>(p, tile_local, &tm, &tn, &row0)) return;
+    ml = min(row0 + tm * BM, p_in.M - BM) - row0;   // may reach into earlier groups
   } else {
     tile_to_mn(p.tile_base + tile_local, p.tiles_m, p.tiles_n, &tm, &tn);
+    ml = min(tm * BM, p.M - BM);
   }
   const int m0 = tm * BM, n0 = tn * BN;
+  const int nl = min(n0, p.N - BN);
   const int kb_begin = blockIdx.y * p.kb_per_split;
   const int kb_end = min(p.kblocks, kb_begin + p.kb_per_split);
 
@@ -566,18 +584,44 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const uint32_t a_voff = (uint32_t)((8 * wave + lrow) * p.lda + lchunk * 16);
   const uint32_t b_voff = (uint32_t)((8 * wave + lrow) * p.ldb + lchunk * 16);
   const __amdgpu_buffer_rsrc_t ars =
-      buffer_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)(p.M - m0) * p.lda);
+      buffer_rsrc(p.a + (int64_t)ml * p.lda, (int64_t)BM * p.lda);
   const __amdgpu_buffer_rsrc_t brs =
-      buffer_rsrc(p.b + (int64_t)n0 * p.ldb, (int64_t)(p.N - n0) * p.ldb);
-  // 128x128 B scales: lane l loads the scale of column block n0 / 128 + l
-  // (clamped to the last block).
-  const uint32_t rbn_voff = (uint32_t)(min(n0 / 128 + lane, (p.N - 1) / 128) * p.rb_s_row * 4);
+      buffer_rsrc(p.b + (int64_t)nl * p.ldb, (int64_t)BN * p.ldb);
+  // Scale slots of this lane.  ra lands transposed per wave row band of 16 TM
+  // rows, in groups of four sub-tiles: LDS slot k = 16 TM h + 64 q + 4 r + v
+  // holds row 16 TM h + 16 (4 q + v) + r, so a lane (fragment row r) finds
+  // the scales of sub-tiles 4q .. 4q + 3 in one 16-byte chunk, and the 16
+  // rows' chunks of one group are 256 consecutive bytes (one conflict-free
+  // pass).  128x128 B scales: lane l loads column block nl / 128 + l
+  // (clamped to the last block); per-row B scales: slot 64 blk + l holds row
+  // 64 blk + l of the window.
+  static_assert(TM % 4 == 0, "scales grouped by four sub-tiles");
+  uint32_t ra_voff[RAI > 0 ? RAI : 1];
+  uint32_t rb_voff[RBI > 0 ? RBI : 1];
+#pragma unroll
+  for (int i = 0; i < RAI; ++i) {
+    const int k = 64 * ((wave + LW * i) % RAB) + lane;
+    const int kb16 = k % (16 * TM);
+    const int row = (k / (16 * TM)) * (16 * TM) + 16 * (4 * (kb16 / 64) + kb16 % 4) + (kb16 % 64) / 4;
+    ra_voff[i] = (uint32_t)(row * p.ra_s_row * 4);
+  }
+#pragma unroll
+  for (int i = 0; i < RBI; ++i) {
+    const int r = MODE == kBlockB128 ? min(nl / 128 + lane, (p.N - 1) / 128)
+                                     : 64 * ((wave + LW * i) % RBB) + lane;
+    rb_voff[i] = (uint32_t)(r * p.rb_s_row * 4);
+  }
+  const float* ra_base = p.ra + (int64_t)ml * p.ra_s_row;
+  const int64_t ra_bytes = ((int64_t)(BM - 1) * p.ra_s_row + 1) * 4;
+  const float* rb_base = MODE == kBlockB128 ? p.rb : p.rb + (int64_t)nl * p.rb_s_row;
+  const int64_t rb_bytes = MODE == kBlockB128 ? ((int64_t)((p.N - 1) / 128) * p.rb_s_row + 1) * 4
+                                              : ((int64_t)(BN - 1) * p.rb_s_row + 1) * 4;
 
-#define FP8BW_ISSUE(kb, st)                                                                  \
-  if (wave < LW)                                                                             \
-  issue_stage<AI, BI, RAI, RBI, RAB, RBB, LW, MODE, TM>(p, (kb), sA[st], sB[st], sRa[st], sRb[st], \
-                                                    ars, brs, a_voff, b_voff, rbn_voff, wave, \
-                                                    lane, m0, n0)
+#define FP8BW_ISSUE(kb, st)                                                                   \
+  if (wave < LW)                                                                              \
+  issue_stage<AI, BI, RAI, RBI, RAB, RBB, LW, MODE>(p, (kb), sA[st], sB[st], sRa[st], sRb[st], \
+                                                    ars, brs, a_voff, b_voff, ra_voff, rb_voff, \
+                                                    ra_base, ra_bytes, rb_base, rb_bytes, wave)
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -662,7 +706,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
         for (int v = 0; v < 4; ++v) sa[4 * q + v] = s4[v];
       }
       if constexpr (MODE == kBlockB128) {
-        const float sbn = sRb[st][(n0 + wn0) / 128 - n0 / 128];
+        const float sbn = sRb[st][(nl + wn0) / 128 - nl / 128];
 #pragma unroll
         for (int i = 0; i < TM; ++i) sa[i] *= sbn;
       } else {
@@ -752,12 +796,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
       pld = p.N;
     }
   }
-  if (m0 + BM <= p.M && n0 + BN <= p.N)
-    store_acc<false, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, m0 + wm0, n0 + wn0, frow, fhalf,
-                                               pbase, pld, pm0, pn0);
+  if (ml == m0 && nl == n0 && m0 + BM <= p.M && n0 + BN <= p.N)
+    store_acc<false, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, m0 + wm0, n0 + wn0, m0, n0, frow,
+                                               fhalf, pbase, pld, pm0, pn0);
   else
-    store_acc<true, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, m0 + wm0, n0 + wn0, frow, fhalf,
-                                              pbase, pld, pm0, pn0);
+    store_acc<true, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, ml + wm0, nl + wn0, m0, n0, frow,
+                                              fhalf, pbase, pld, pm0, pn0);
 }
 #undef FP8BW_ISSUE
 
@@ -872,13 +916,23 @@ int gemm_num_configs() { return kNumCfgs; }
 bool gemm_config_ok(const GemmProblem& p, int cfg) {
   if (cfg < 0 || cfg >= kNumCfgs) return false;
   if (kCfgs[cfg].kind == 1) {
-    // The large-tile kernels load whole 128-byte K blocks (no K tail) and
-    // address a row tile of A or B (at most 256 rows) and a column of B
-    // block scales with signed 32-bit buffer offsets.
+    // The large-tile kernels load whole 128-byte K blocks (no K tail), need
+    // at least one whole tile in each dimension (an edge tile's operand
+    // window moves back inside the matrix), and address a row tile of A or
+    // B (at most 256 rows) and the scales of a tile with signed 32-bit
+    // buffer offsets.
     if (p.K % 128) return false;
+    if (p.M < kCfgs[cfg].bm || p.N < kCfgs[cfg].bn) return false;
+    // 128x128 B scales: a wave's 64 columns must stay inside one scale
+    // block when the last column tile moves back to end at row N - 1.
+    if (p.mode == kBlockB128 && p.N % 64) return false;
     const int64_t lim = (int64_t)1 << 31;
     if (256 * p.lda + p.K >= lim || 256 * p.ldb + p.K >= lim) return false;
-    if (((p.N + 127) / 128) * p.rb_s_row * 4 >= lim) return false;
+    if (p.mode != kTensorwise) {
+      if (256 * p.ra_s_row * 4 >= lim) return false;
+      const int64_t rb_rows = p.mode == kBlockB128 ? (p.N + 127) / 128 : 256;
+      if (rb_rows * p.rb_s_row * 4 >= lim) return false;
+    }
   }
   return true;
 }
@@ -1051,6 +1105,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
   a.lda = p.lda;
   a.ldb = p.ldb;
   a.ldo = p.ldo;
+  a.ra_s_row = p.ra_s_row;
   a.ra_s_kb = p.ra_s_kb;
   a.rb_s_row = p.rb_s_row;
   a.rb_s_kb = p.rb_s_kb;
@@ -1107,15 +1162,22 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
 // Grouped GEMM launch (see GemmArgs::groups).  The grid covers the worst
 // case, sum over groups of ceil(M_g / BM) <= ceil(M / BM) + groups row tiles,
 // times the column tiles; workgroups past the last tile return at once.
+// Problems with fewer rows or columns than a large tile run on the
+// small-tile kernel, which clamps its loads to each group's rows.
+static int grouped_config(const GemmProblem& p) {
+  if (p.N >= 256 && gemm_config_ok(p, 3)) return 3;
+  if (p.N >= 128 && gemm_config_ok(p, 2)) return 2;
+  return (p.M >= 128 && p.N >= 128) ? 0 : 1;
+}
+
 bool grouped_gemm_ok(const GemmProblem& p, int groups) {
-  if (groups <= 0 || p.K % 128 || p.N < 128) return false;
-  return gemm_config_ok(p, p.N >= 256 ? 3 : 2);
+  return groups > 0 && p.K % 128 == 0;
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, int groups, const int* group_end,
                                int64_t b_s_group, int64_t rb_s_group, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  const int cfg = p.N >= 256 ? 3 : 2;
+  const int cfg = grouped_config(p);
   const int bm = kCfgs[cfg].bm, bn = kCfgs[cfg].bn;
   GemmArgs a = {};
   a.a = (const uint8_t*)p.a;
@@ -1126,6 +1188,7 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, int groups, const int* grou
   a.lda = p.lda;
   a.ldb = p.ldb;
   a.ldo = p.ldo;
+  a.ra_s_row = p.ra_s_row;
   a.ra_s_kb = p.ra_s_kb;
   a.rb_s_row = p.rb_s_row;
   a.rb_s_kb = p.rb_s_kb;
@@ -1135,13 +1198,18 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, int groups, const int* grou
   a.kblocks = (int)(p.K / 128);
   a.kb_per_split = a.kblocks;
   a.tiles_n = (int)((p.N + bn - 1) / bn);
-  a.tiles_m = 0;
   a.groups = groups;
   a.group_end = group_end;
   a.b_s_group = b_s_group;
   a.rb_s_group = rb_s_group;
-  const int64_t ntiles = ((p.M + bm - 1) / bm + groups) * a.tiles_n;
-  return launch_v2_cfg(cfg, a, p.mode, (int)ntiles, 1, p.out_kind, stream);
+  const int64_t tiles_m = (p.M + bm - 1) / bm + groups;
+  if (kCfgs[cfg].kind == 0) {
+    a.tiles_m = (int)tiles_m;   // grid only; each tile's group sets its own
+    return cfg == 0 ? launch_mode<128, 128>(a, p.mode, 1, p.out_kind, stream)
+                    : launch_mode<64, 64>(a, p.mode, 1, p.out_kind, stream);
+  }
+  a.tiles_m = 0;
+  return launch_v2_cfg(cfg, a, p.mode, (int)(tiles_m * a.tiles_n), 1, p.out_kind, stream);
 }
 
 }  // namespace fp8bw

@@ -150,11 +150,17 @@ int fp8_tensorwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x
  * ([REPRO] What Changed: the blockwise GEMM on the same codes and
  * reciprocal scales as the dequantized matmul; out = A . B^T as F.linear).
  *
- *   a   device E4M3 [M, K], lda; ra: 1x128 scales of A, ra[m + kb*ra_s_kb]
- *       (column-major; ra_s_kb >= M).
+ *   a   device E4M3 [M, K], lda; ra: 1x128 scales of A,
+ *       ra[m*ra_s_row + kb*ra_s_kb].
  *   b   device E4M3 [N, K], ldb.  b_block selects rb's meaning:
  *         FP8BW_BLOCK_128x128: rb[(n/128)*rb_s_row + kb*rb_s_kb]  (fwd, dgrad)
- *         FP8BW_BLOCK_1x128:   rb[n + kb*rb_s_kb], rb_s_row must be 1 (wgrad)
+ *         FP8BW_BLOCK_1x128:   rb[n*rb_s_row + kb*rb_s_kb]        (wgrad)
+ *       Scale strides: the column-major layout the quantizers write
+ *       (s_row = 1, s_kb >= rows: [INTEG] Summary) is the fast one; any
+ *       other non-overlapping nested strides (row-major, transposed or
+ *       padded views) are accepted as they are, without a copy.  Strides
+ *       that alias (one stride does not span the other dimension's whole
+ *       extent) or are negative give FP8BW_ERR_LAYOUT.
  *   out device [M, N] bf16 (RNE from the fp32 accumulator) or fp32, ldo.
  *   K % 128 == 0 (K blocks may number anything, e.g. 1001 or 1002).
  *   Each K block is accumulated in fp32 by the matrix cores and rescaled in
@@ -248,9 +254,9 @@ int fp8_scaled_gemm_tensorwise_bias(const void* a, int64_t lda, const float* ra,
  *               are not written.
  *   b_s_group   >= (N-1)*ldb + K, a multiple of 16 (distinct weights).
  *   rb_s_group  large enough that groups' scale grids do not overlap.
- *   Requires K % 128 == 0, N >= 128 and 256*lda + K, 256*ldb + K < 2^31
- *   (a 256-row tile is addressed with signed 32-bit byte offsets; else
- *   FP8BW_ERR_UNSUPPORTED); no split-K, no workspace.
+ *   Requires K % 128 == 0; no split-K, no workspace.  Problems with
+ *   M >= 256 and N >= 128 (and 256*lda + K, 256*ldb + K < 2^31) run on the
+ *   large-tile kernels, others on the small-tile kernel.
  */
 int fp8_scaled_grouped_gemm_blockwise(const void* a, int64_t lda, const float* ra,
                                       int64_t ra_s_kb, const void* b, int64_t ldb,

@@ -121,9 +121,10 @@ def test_gemm_validation(lib):
     assert _gemm(lib, lda=128) == LAYOUT                 # lda < K
     assert _gemm(lib, ldb=264) == LAYOUT                 # not a multiple of 16
     assert _gemm(lib, ldo=100) == LAYOUT                 # ldo < N
-    assert _gemm(lib, ra_s_row=2) == LAYOUT              # ra must be column-major
+    assert _gemm(lib, ra_s_row=2) == LAYOUT              # row 32 meets (row 0, kb 1)
     assert _gemm(lib, ra_s_kb=32) == LAYOUT              # aliases rows of ra
-    assert _gemm(lib, b_block=0, rb_s_row=2, rb_s_kb=256) == LAYOUT   # 1x128 rb column-major
+    assert _gemm(lib, b_block=0, rb_s_row=2, rb_s_kb=200) == LAYOUT   # 1x128 rb: row 100 aliases
+    assert _gemm(lib, b_block=0, rb_s_row=-2, rb_s_kb=256) == LAYOUT  # negative stride
     assert _gemm(lib, rb_s_row=1, rb_s_kb=0) == LAYOUT   # 128x128 rb: aliases
     assert _gemm(lib, M=0, a=None, b=None, out=None) == OK
     assert _gemm(lib, "fp8_scaled_gemm_blockwise_cfg", config=99) == UNSUP
@@ -169,7 +170,6 @@ def test_grouped_gemm_validation(lib):
     assert _grouped(lib, b_s_group=100) == LAYOUT           # groups' weights overlap
     assert _grouped(lib, ra_s_kb=8) == LAYOUT               # ra not column-major
     assert _grouped(lib, rb_s_group=1) == LAYOUT            # groups' scales overlap
-    assert _grouped(lib, N=64, ldo=64) == UNSUP             # N < 128
     assert _grouped(lib, M=0, a=None, out=None, group_end=None) == OK
 
 

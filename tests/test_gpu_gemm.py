@@ -31,14 +31,21 @@ def _random_codes(rng, shape):
     return c
 
 
-def _run_blockwise(dev, aq, ar, bq, br, b_block, out_dtype, what, config=None, splits=None):
-    say("gemm blockwise", what, aq.shape, bq.shape, b_block, out_dtype, config, splits)
+def _run_blockwise(dev, aq, ar, bq, br, b_block, out_dtype, what, config=None, splits=None,
+                   ldo_pad=0):
+    """One GEMM call against the oracle; with ldo_pad the output is a view
+    of a NaN-filled [M, N + ldo_pad] buffer whose padding must stay NaN."""
+    say("gemm blockwise", what, aq.shape, bq.shape, b_block, out_dtype, config, splits, ldo_pad)
     od = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    M, N = aq.shape[0], bq.shape[0]
+    buf = torch.full((M, N + ldo_pad), float("nan"), dtype=od, device=dev)
     out = fp8.fp8_scaled_gemm_blockwise(_up_codes(aq, dev), _up_scales_colmajor(ar, dev),
                                         _up_codes(bq, dev), _up_scales_colmajor(br, dev),
                                         b_block=b_block, out_dtype=od, config=config,
-                                        splits=splits)
+                                        splits=splits, out=buf[:, :N])
     torch.cuda.synchronize()
+    if ldo_pad:
+        assert torch.isnan(buf[:, N:].float()).all(), f"{what}: wrote past N"
     ref, S = gemm.blockwise_gemm(aq, ar, bq, br, b_block, with_bound=True)
     return check_gemm_output(host_f32(out), ref, S, aq.shape[1] // 128, out_dtype, what)
 
@@ -83,22 +90,90 @@ def test_power_of_two_scale_probe(gpu):
         _run_blockwise(gpu, aq, ar, bq, br, b_block, "f32", f"pow2 probe {b_block}")
 
 
-def test_every_config_and_split(gpu):
+# Large-tile configurations and their tile sizes (BM, BN): they need M >= BM
+# and N >= BN (an edge tile's operand window moves back inside the matrix).
+LARGE_TILES = {2: (256, 128), 3: (256, 256)}
+
+
+def _config_accepts(cfg, M, N, b_block):
+    bm, bn = LARGE_TILES.get(cfg, (1, 1))
+    if cfg in LARGE_TILES and b_block == "128x128" and N % 64:
+        return False      # a wave's 64 columns must keep one B scale block
+    return M >= bm and N >= bn
+
+
+@pytest.mark.parametrize("mn,pad", [((200, 300), 0), ((300, 448), 0), ((300, 401), 3)])
+def test_every_config_and_split(gpu, mn, pad):
     """Force every tile configuration and several split-K counts (a kernel
-    variant can be wrong where the others are right)."""
-    rng = np.random.default_rng(4)
-    M, N, kb = 200, 300, 8
+    variant can be wrong where the others are right).  300 x 448 and
+    300 x 401 give the large-tile kernels ragged edge tiles in both
+    dimensions (at 401 columns, per-row B scales, an output row stride of
+    404 and column quads that do not start on a multiple of 4); a large
+    configuration forced on a problem it does not take is refused."""
+    rng = np.random.default_rng(4 + mn[0] + mn[1])
+    M, N = mn
+    kb = 8
     aq = _random_codes(rng, (M, 128 * kb))
     bq = _random_codes(rng, (N, 128 * kb))
     ar = rng.uniform(0.01, 0.02, (M, kb)).astype(np.float32)
     for b_block in ("128x128", "1x128"):
-        nbr = N if b_block == "1x128" else 3
+        nbr = N if b_block == "1x128" else -(-N // 128)
         br = rng.uniform(0.01, 0.02, (nbr, kb)).astype(np.float32)
         for cfg in range(fp8.fp8bw_gemm_num_configs()):
+            if not _config_accepts(cfg, M, N, b_block):
+                with pytest.raises(fp8.FP8BWError, match="UNSUPPORTED"):
+                    _run_blockwise(gpu, aq, ar, bq, br, b_block, "f32", f"cfg{cfg} refused",
+                                   config=cfg, splits=1)
+                continue
             for splits in (1, 2, 3, 8):
                 for od in ("bf16", "f32"):
-                    _run_blockwise(gpu, aq, ar, bq, br, b_block, od, f"cfg{cfg} split{splits}",
-                                   config=cfg, splits=splits)
+                    _run_blockwise(gpu, aq, ar, bq, br, b_block, od,
+                                   f"M{M} N{N} {b_block} cfg{cfg} split{splits}", config=cfg,
+                                   splits=splits, ldo_pad=pad)
+
+
+def _scale_view(r, layout, dev):
+    """Logical fp32 [ni, nj] on the device in a given memory layout."""
+    r = np.asarray(r, np.float32)
+    ni, nj = r.shape
+    if layout == "colmajor":
+        return _up_scales_colmajor(r, dev)
+    if layout == "rowmajor":
+        return torch.from_numpy(np.ascontiguousarray(r)).to(dev)
+    if layout == "rowmajor_padded":
+        buf = torch.full((ni, nj + 3), float("nan"), dtype=torch.float32, device=dev)
+        buf[:, :nj] = torch.from_numpy(r).to(dev)
+        return buf[:, :nj]
+    if layout == "colmajor_padded":
+        buf = torch.full((nj, ni + 5), float("nan"), dtype=torch.float32, device=dev)
+        buf[:, :ni] = torch.from_numpy(np.ascontiguousarray(r.T)).to(dev)
+        return buf[:, :ni].t()
+    raise ValueError(layout)
+
+
+@pytest.mark.parametrize("layout", ["rowmajor", "rowmajor_padded", "colmajor_padded"])
+def test_scale_strides_any_nested_layout(gpu, layout):
+    """A and B scales given as row-major, padded row-major and padded
+    column-major views (no copies), for both B recipes, on the small-tile
+    and the large-tile kernels (ragged 300 x 448), against the oracle on
+    the logical scale grids."""
+    rng = np.random.default_rng(17)
+    M, N, kb = 300, 448, 6
+    aq = _random_codes(rng, (M, 128 * kb))
+    bq = _random_codes(rng, (N, 128 * kb))
+    ar = (rng.uniform(0.5, 2.0, (M, kb)) * 2.0 ** -8).astype(np.float32)
+    for b_block in ("128x128", "1x128"):
+        nbr = N if b_block == "1x128" else -(-N // 128)
+        br = (rng.uniform(0.5, 2.0, (nbr, kb)) * 2.0 ** -9).astype(np.float32)
+        ref, S = gemm.blockwise_gemm(aq, ar, bq, br, b_block, with_bound=True)
+        for cfg in (None, 0, 1, 2, 3):
+            say("gemm scale strides", layout, b_block, cfg)
+            out = fp8.fp8_scaled_gemm_blockwise(_up_codes(aq, gpu), _scale_view(ar, layout, gpu),
+                                                _up_codes(bq, gpu), _scale_view(br, layout, gpu),
+                                                b_block=b_block, out_dtype=torch.float32,
+                                                config=cfg, splits=None if cfg is None else 1)
+            torch.cuda.synchronize()
+            check_gemm_output(host_f32(out), ref, S, kb, "f32", f"strides {layout} {b_block} cfg{cfg}")
 
 
 def test_canary_output_and_strided_b_scales(gpu):
@@ -164,16 +239,24 @@ def test_long_k_1000_1001_1002_blocks(gpu):
 @pytest.mark.parametrize("splits", [1, 7, 13, 64])
 def test_long_k_forced_splits(gpu, splits):
     """K = 128128 (1001 blocks, 7 x 11 x 13) with forced split counts that do
-    and do not divide the block count."""
+    and do not divide the block count, on every tile configuration (M = 320:
+    the 256-row kernels get a ragged second row tile)."""
     rng = np.random.default_rng(splits)
-    M, N, K = 64, 256, 128128
+    M, N, K = 320, 256, 128128
     aq = _random_codes(rng, (M, K))
     bq = _random_codes(rng, (N, K))
     ar = rng.uniform(1e-3, 2e-3, (M, K // 128)).astype(np.float32)
     br = rng.uniform(1e-3, 2e-3, (2, K // 128)).astype(np.float32)
+    ref, S = gemm.blockwise_gemm(aq, ar, bq, br, "128x128", with_bound=True)
+    args = (_up_codes(aq, gpu), _up_scales_colmajor(ar, gpu), _up_codes(bq, gpu),
+            _up_scales_colmajor(br, gpu))
     for cfg in range(fp8.fp8bw_gemm_num_configs()):
-        _run_blockwise(gpu, aq, ar, bq, br, "128x128", "f32", f"long-K splits={splits} cfg{cfg}",
-                       config=cfg, splits=splits)
+        say("gemm long-K forced", splits, cfg)
+        out = fp8.fp8_scaled_gemm_blockwise(*args, out_dtype=torch.float32, config=cfg,
+                                            splits=splits)
+        torch.cuda.synchronize()
+        check_gemm_output(host_f32(out), ref, S, K // 128, "f32",
+                          f"long-K splits={splits} cfg{cfg}")
 
 
 def _tensorwise_case(dev, M, N, K, out_dtype, seed):

@@ -80,6 +80,16 @@ def test_grouped_moe_like_sampled(gpu):
     _case(gpu, G, M, N, K, ends, "bf16", seed=53, sample=sample)
 
 
+@pytest.mark.parametrize("mn", [(200, 384), (520, 64), (100, 96)])
+def test_grouped_small_problems_use_the_small_tiles(gpu, mn):
+    """Fewer rows than a 256-row tile, or fewer columns than 128: the
+    small-tile kernel runs the groups (loads clamped to each group's rows),
+    with an empty group and a group smaller than a tile."""
+    M, N = mn
+    ends = [M // 4, M // 4, M // 2 + 3, M]
+    _case(gpu, 4, M, N, 512, ends, "f32", seed=56 + M)
+
+
 def test_grouped_malformed_table_is_clamped(gpu):
     """Decreasing ends and ends past M are clamped to [previous end, M]."""
     _case(gpu, 4, 512, 256, 256, [200, 100, 9999, 50], "f32", seed=54)
