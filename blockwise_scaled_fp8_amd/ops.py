@@ -84,6 +84,32 @@ def _check_shape(t, shape, name):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+CODE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _check_codes_out(t, shape, name):
+    """A caller-provided code buffer: E4M3 bytes, row-major rows."""
+    _check_shape(t, shape, name)
+    if t.dtype not in CODE_DTYPES:
+        raise ValueError(f"{name} must be uint8 or float8_e4m3fn, got {t.dtype}")
+    _rowmajor(t, name)
+
+
+def _check_scales(t, shape, name):
+    """fp32 reciprocal scales of a given logical shape (any strides; the
+    library checks that they do not overlap)."""
+    _check_shape(t, shape, name)
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+
+
+def _check_out(t, shape, name="out"):
+    _check_shape(t, shape, name)
+    if t.dtype not in OUT_DTYPES:
+        raise ValueError(f"{name} must be bfloat16 or float32, got {t.dtype}")
+    _rowmajor(t, name)
+
+
 @_on_tensor_device
 def fp8_blockwise_quant(x, block="1x128", transpose=False, q=None, recip=None):
     """Quantize bf16 x[rows, cols] to E4M3 codes with per-block reciprocal scales.
@@ -99,11 +125,11 @@ def fp8_blockwise_quant(x, block="1x128", transpose=False, q=None, recip=None):
     qshape = (cols, rows) if transpose else (rows, cols)
     if q is None:
         q = torch.empty(qshape, dtype=torch.uint8, device=x.device)
-    _check_shape(q, qshape, "q")
+    _check_codes_out(q, qshape, "q")
     ni, nj = scale_grid(rows, cols, block, transpose)
     if recip is None:
         recip = colmajor_empty(ni, nj, x.device)
-    _check_shape(recip, (ni, nj), "recip")
+    _check_scales(recip, (ni, nj), "recip")
     check(lib.fp8_blockwise_quant(x.data_ptr(), rows, cols, x.stride(0), BLOCKS[block],
                                   int(bool(transpose)), q.data_ptr(), q.stride(0),
                                   recip.data_ptr(), recip.stride(0), recip.stride(1), _stream(x)))
@@ -125,16 +151,16 @@ def fp8_blockwise_quant_dual(x, block="1x128", q=None, recip=None, qt=None, reci
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if qt is None:
         qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
-    _check_shape(q, (rows, cols), "q")
-    _check_shape(qt, (cols, rows), "qt")
+    _check_codes_out(q, (rows, cols), "q")
+    _check_codes_out(qt, (cols, rows), "qt")
     ni, nj = scale_grid(rows, cols, block, False)
     ti, tj = scale_grid(rows, cols, block, True)
     if recip is None:
         recip = colmajor_empty(ni, nj, x.device)
     if recip_t is None:
         recip_t = colmajor_empty(ti, tj, x.device)
-    _check_shape(recip, (ni, nj), "recip")
-    _check_shape(recip_t, (ti, tj), "recip_t")
+    _check_scales(recip, (ni, nj), "recip")
+    _check_scales(recip_t, (ti, tj), "recip_t")
     check(lib.fp8_blockwise_quant_dual(x.data_ptr(), rows, cols, x.stride(0), BLOCKS[block],
                                        q.data_ptr(), q.stride(0), recip.data_ptr(), recip.stride(0),
                                        recip.stride(1), qt.data_ptr(), qt.stride(0),
@@ -149,11 +175,16 @@ def fp8_tensorwise_quant(x, q=None, recip=None):
     lib = load_library()
     _need_cuda(x)
     _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
     rows, cols = x.shape
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    _check_codes_out(q, (rows, cols), "q")
     if recip is None:
         recip = torch.empty(1, dtype=torch.float32, device=x.device)
+    if recip.numel() != 1 or recip.dtype != torch.float32:
+        raise ValueError("recip must be a one-element float32 tensor")
     nws = lib.fp8bw_tensorwise_quant_ws_bytes(rows, cols)
     ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
     check(lib.fp8_tensorwise_quant(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(), q.stride(0),
@@ -186,11 +217,13 @@ def fp8_scaled_gemm_blockwise(a, ra, b, rb, b_block="128x128", out_dtype=torch.b
     N = b.shape[0]
     _check_codes(a, b, K)
     kb = _cdiv(K, 128)
-    _check_shape(ra, (M, kb), "ra")
-    _check_shape(rb, (N if b_block == "1x128" else _cdiv(N, 128), kb), "rb")
+    if b_block not in BLOCKS:
+        raise ValueError(f"b_block must be one of {sorted(BLOCKS)}")
+    _check_scales(ra, (M, kb), "ra")
+    _check_scales(rb, (N if b_block == "1x128" else _cdiv(N, 128), kb), "rb")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    _check_shape(out, (M, N), "out")
+    _check_out(out, (M, N))
     args = (a.data_ptr(), a.stride(0), ra.data_ptr(), ra.stride(0), ra.stride(1),
             b.data_ptr(), b.stride(0), rb.data_ptr(), rb.stride(0), rb.stride(1),
             BLOCKS[b_block], M, N, K, out.data_ptr(), out.stride(0), OUT_DTYPES[out.dtype])
@@ -235,9 +268,11 @@ def fp8_scaled_gemm_tensorwise(a, ra, b, rb, out_dtype=torch.bfloat16, out=None,
     _check_codes(a, b, K)
     if ra.numel() != 1 or rb.numel() != 1:
         raise ValueError("tensorwise scales are one-element tensors")
+    if ra.dtype != torch.float32 or rb.dtype != torch.float32:
+        raise ValueError("tensorwise scales are float32")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    _check_shape(out, (M, N), "out")
+    _check_out(out, (M, N))
     _check_bias(bias, N, a.device)
     if bias is not None:
         check(lib.fp8_scaled_gemm_tensorwise_bias(a.data_ptr(), a.stride(0), ra.data_ptr(),
@@ -267,13 +302,15 @@ def fp8_scaled_grouped_gemm_blockwise(a, ra, b, rb, group_end, out_dtype=torch.b
     if a.dtype != torch.uint8 or b.dtype != torch.uint8:
         raise ValueError("codes are uint8 tensors")
     kb = _cdiv(K, 128)
-    _check_shape(ra, (M, kb), "ra")
-    _check_shape(rb, (G, _cdiv(N, 128), kb), "rb")
+    _check_scales(ra, (M, kb), "ra")
+    if ra.stride(0) != 1 and M > 1:
+        raise ValueError("ra of the grouped GEMM must be column-major (unit row stride)")
+    _check_scales(rb, (G, _cdiv(N, 128), kb), "rb")
     if group_end.dtype != torch.int32 or group_end.shape != (G,) or group_end.stride(0) != 1:
         raise ValueError("group_end must be a contiguous int32 [G] tensor")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    _check_shape(out, (M, N), "out")
+    _check_out(out, (M, N))
     check(lib.fp8_scaled_grouped_gemm_blockwise(
         a.data_ptr(), a.stride(0), ra.data_ptr(), ra.stride(1), b.data_ptr(), b.stride(1),
         b.stride(0), rb.data_ptr(), rb.stride(1), rb.stride(2), rb.stride(0), G,

@@ -77,7 +77,16 @@ def gemm_gamma(kblocks):
     return MFMA_BLOCK_REL + 2.0 * (2 + kblocks) * 2.0 ** -24
 
 
-def check_gemm_output(got, ref64, bound, kblocks, out_dtype, what, rel_fro_max=1e-3):
+# Largest fraction of bf16 output elements allowed to fall outside 2 bf16
+# ulp of the oracle and pass only by the cancellation floor.  Measured on
+# every GPU parity case: at most 0.33% (random codes over the whole E4M3
+# range, tiny outputs), at most 0.13% on the linear shapes with Gaussian
+# data, K from 128 to 128256.
+MAX_FLOOR_FRAC = 0.01
+
+
+def check_gemm_output(got, ref64, bound, kblocks, out_dtype, what, rel_fro_max=1e-3,
+                      max_floor_frac=MAX_FLOOR_FRAC):
     """Parity bar for GEMM outputs against the oracle's float64 result.
 
     fp32 out: relative Frobenius error <= 1e-3 against the oracle's fp32
@@ -89,8 +98,9 @@ def check_gemm_output(got, ref64, bound, kblocks, out_dtype, what, rel_fro_max=1
     gamma * S + 1 ulp; the relative Frobenius error against that bf16
     reference must also stay <= 1e-3.  (The bf16 cast alone moves the
     output ~1.6e-3 in relative Frobenius norm, so the 1e-3 bar is only
-    meaningful before the cast.)  Returns (#elements that needed the
-    floor, relative Frobenius error)."""
+    meaningful before the cast.)  The number of bf16 elements that needed
+    the floor is printed and must stay within max_floor_frac of the output.
+    Returns (#elements that needed the floor, relative Frobenius error)."""
     from oracle import e4m3, metrics
     got = np.asarray(got, dtype=np.float64)
     ref64 = np.asarray(ref64, dtype=np.float64)
@@ -109,7 +119,12 @@ def check_gemm_output(got, ref64, bound, kblocks, out_dtype, what, rel_fro_max=1
         floor = err <= gam * bound + metrics.bf16_ulp(got)
         bad = ~(within2 | floor)
         floor_used = int(np.count_nonzero(~within2 & floor))
+    n = int(got.size)
+    print(f"[floor] {what}: {floor_used} of {n} elements outside 2 bf16 ulp, within the floor "
+          f"({floor_used / max(n, 1):.3%}); rel. Frobenius {rf:.3e}", flush=True)
     assert rf <= rel_fro_max, f"{what}: relative Frobenius error {rf:.3e} > {rel_fro_max}"
+    assert floor_used <= max_floor_frac * n, (
+        f"{what}: {floor_used} of {n} elements needed the floor (> {max_floor_frac:.2%})")
     if bad.any():
         idx = tuple(b[0] for b in np.nonzero(bad))
         raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance; first {idx}: "

@@ -88,3 +88,31 @@ def test_training_token_count_checked_in_forward():
     with torch.no_grad():
         y = m(_meta(2, 50, 256, grad=False))
     assert y.shape == (2, 50, 128)
+
+
+def test_binding_rejects_wrong_dtypes_and_strides():
+    """Caller-provided codes, scales and outputs are checked for dtype and
+    layout before any pointer reaches the library (a bf16 scale tensor read
+    as fp32, or a column-strided output, would address the wrong memory)."""
+    from blockwise_scaled_fp8_amd import ops
+    codes = torch.zeros((4, 32), dtype=torch.uint8)
+    ops._check_codes_out(codes, (4, 32), "q")
+    ops._check_codes_out(codes.view(torch.float8_e4m3fn), (4, 32), "q")
+    with pytest.raises(ValueError, match="uint8 or float8"):
+        ops._check_codes_out(codes.to(torch.int8), (4, 32), "q")
+    with pytest.raises(ValueError, match="unit column stride"):
+        ops._check_codes_out(torch.zeros((32, 4), dtype=torch.uint8).t(), (4, 32), "q")
+    with pytest.raises(ValueError, match="shape"):
+        ops._check_codes_out(codes, (4, 16), "q")
+    sc = torch.zeros((4, 2), dtype=torch.float32)
+    ops._check_scales(sc, (4, 2), "ra")
+    ops._check_scales(sc.t().contiguous().t(), (4, 2), "ra")      # any strides
+    with pytest.raises(ValueError, match="float32"):
+        ops._check_scales(sc.to(torch.bfloat16), (4, 2), "ra")
+    out = torch.zeros((4, 8), dtype=torch.bfloat16)
+    ops._check_out(out, (4, 8))
+    ops._check_out(out.float(), (4, 8))
+    with pytest.raises(ValueError, match="bfloat16 or float32"):
+        ops._check_out(out.half(), (4, 8))
+    with pytest.raises(ValueError, match="unit column stride"):
+        ops._check_out(torch.zeros((8, 4), dtype=torch.float32).t(), (4, 8))
