@@ -20,6 +20,7 @@ from .ops import (  # noqa: F401
     fp8_scaled_gemm_tensorwise,
     fp8_scaled_grouped_gemm_blockwise,
     fp8_tensorwise_quant,
+    fp8_tensorwise_quant_noalloc,
     fp8bw_gemm_num_configs,
     linear_saved_bytes,
     linear_workspace,

@@ -25,6 +25,8 @@ PROTOTYPES = {
     "fp8bw_tensorwise_quant_ws_bytes": (c_size, [c_i64, c_i64]),
     "fp8_tensorwise_quant": (c_int, [c_ptr, c_i64, c_i64, c_i64, c_ptr, c_i64, c_ptr, c_ptr,
                                      c_size, c_ptr]),
+    "fp8_tensorwise_quant_noalloc": (c_int, [c_ptr, c_i64, c_i64, c_i64, c_ptr, c_i64, c_ptr,
+                                             c_ptr]),
     "fp8bw_gemm_blockwise_ws_bytes": (c_size, [c_i64, c_i64, c_i64]),
     "fp8_scaled_gemm_blockwise": (c_int, [c_ptr, c_i64, c_ptr, c_i64, c_i64, c_ptr, c_i64, c_ptr,
                                           c_i64, c_i64, c_int, c_i64, c_i64, c_i64, c_ptr, c_i64,

@@ -186,6 +186,25 @@ FP8BW_API int fp8_tensorwise_quant(const void* x, int64_t rows, int64_t cols, in
                     "fp8_tensorwise_quant");
 }
 
+FP8BW_API int fp8_tensorwise_quant_noalloc(const void* x, int64_t rows, int64_t cols,
+                                           int64_t ld_x, void* q, int64_t ld_q, float* recip,
+                                           void* stream) {
+  int st = check_quant_common(x, rows, cols, ld_x, q, ld_q, cols);
+  if (st != FP8BW_OK) return st;
+  if (!recip) return fail(FP8BW_ERR_NULL, "recip must be non-null");
+  if (!aligned(recip, 4)) return fail(FP8BW_ERR_ALIGN, "recip must be 4-byte aligned");
+  // The partials always fit the library's array (their count is capped);
+  // the check guards the invariant.
+  const int64_t r = (rows == 0 || cols == 0) ? 0 : rows;
+  const int64_t c = (rows == 0 || cols == 0) ? 0 : cols;
+  if (fp8bw::tensorwise_partials(r, c) > fp8bw::kMaxTensorwisePartials)
+    return fail(FP8BW_ERR_WORKSPACE, "needs more than the %d partials of the library's scratch",
+                fp8bw::kMaxTensorwisePartials);
+  return hip_status(fp8bw::launch_quant_tensorwise_noalloc(x, r, c, ld_x, q, ld_q, recip,
+                                                           (hipStream_t)stream),
+                    "fp8_tensorwise_quant_noalloc");
+}
+
 // ---------------------------------------------------------------------------
 // GEMM.
 

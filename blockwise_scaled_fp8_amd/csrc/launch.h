@@ -32,11 +32,19 @@ hipError_t launch_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t 
                              void* q, int64_t ld_q, float* recip, int64_t rs_row, int64_t rs_kb,
                              void* qt, int64_t ld_qt, float* recip_t, int64_t rst_row,
                              int64_t rst_kb, hipStream_t stream);
-// Per-tensor: partial amax into ws (n_partials floats), then quantize.
+// Per-tensor: partial amax into ws (n_partials floats, at most
+// kMaxTensorwisePartials), then quantize.
+constexpr int kMaxTensorwisePartials = 1024;
+constexpr int kMaxDevices = 64;
 int tensorwise_partials(int64_t rows, int64_t cols);
 hipError_t launch_quant_tensorwise(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
                                    void* q, int64_t ld_q, float* recip, float* ws,
                                    hipStream_t stream);
+// The same with the partials in the library's own per-device array (no
+// workspace; calls that overlap on one GPU race on it).
+hipError_t launch_quant_tensorwise_noalloc(const void* x, int64_t rows, int64_t cols,
+                                           int64_t ld_x, void* q, int64_t ld_q, float* recip,
+                                           hipStream_t stream);
 
 // ---- GEMM (gemm.hip) ----
 enum ScaleMode { kBlockB128 = 0, kBlockB1x128 = 1, kTensorwise = 2 };

@@ -16,6 +16,8 @@
 // address and have their values masked before use, so no load sits behind a
 // branch and the compiler's waits stay exact.
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -324,7 +326,7 @@ int tensorwise_partials(int64_t rows, int64_t cols) {
   const int64_t chunks = rows * (cols / 8);
   int64_t p = (chunks + 256 * 8 - 1) / (256 * 8);
   if (p < 1) p = 1;
-  if (p > 1024) p = 1024;
+  if (p > kMaxTensorwisePartials) p = kMaxTensorwisePartials;
   return (int)p;
 }
 
@@ -339,6 +341,49 @@ hipError_t launch_quant_tensorwise(const void* x, int64_t rows, int64_t cols, in
   hipLaunchKernelGGL(quant_tensorwise_kernel, dim3(p), dim3(256), 0, stream, (const uint16_t*)x,
                      rows, cols, ld_x, (uint8_t*)q, ld_q, recip, (const float*)ws, p);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free per-tensor quantization: the partial amaxes live in a
+// library-owned device array instead of caller workspace.  Each GPU the
+// library runs on holds its own copy of `scratch` (4 KiB) until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address on each GPU comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// passed to the kernels.  Every call on a GPU shares the array; the amax
+// pass writes every partial the quantize pass reads, so nothing needs
+// clearing between calls, but two calls that overlap on one GPU (different
+// streams) race on it.
+static __device__ __align__(256) float scratch[kMaxTensorwisePartials];
+
+static std::mutex g_scratch_mu;
+static float* g_scratch_dev[kMaxDevices];   // guarded by g_scratch_mu
+
+static hipError_t scratch_of_current_device(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = (float*)ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_quant_tensorwise_noalloc(const void* x, int64_t rows, int64_t cols,
+                                           int64_t ld_x, void* q, int64_t ld_q, float* recip,
+                                           hipStream_t stream) {
+  if (tensorwise_partials(rows, cols) > kMaxTensorwisePartials) return hipErrorInvalidValue;
+  float* ws = nullptr;
+  const hipError_t e = scratch_of_current_device(&ws);
+  if (e != hipSuccess) return e;
+  return launch_quant_tensorwise(x, rows, cols, ld_x, q, ld_q, recip, ws, stream);
 }
 
 }  // namespace fp8bw

@@ -192,6 +192,25 @@ def fp8_tensorwise_quant(x, q=None, recip=None):
     return q, recip
 
 
+@_on_tensor_device
+def fp8_tensorwise_quant_noalloc(x, q, recip):
+    """fp8_tensorwise_quant with no workspace: the library keeps the partial
+    amaxes in its own per-device array.  q (uint8 like x) and recip (fp32
+    [1]) are the caller's; nothing is allocated here or in the library."""
+    lib = load_library()
+    _need_cuda(x)
+    _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    rows, cols = x.shape
+    _check_codes_out(q, (rows, cols), "q")
+    if recip.numel() != 1 or recip.dtype != torch.float32:
+        raise ValueError("recip must be a one-element float32 tensor")
+    check(lib.fp8_tensorwise_quant_noalloc(x.data_ptr(), rows, cols, x.stride(0), q.data_ptr(),
+                                           q.stride(0), recip.data_ptr(), _stream(x)))
+    return q, recip
+
+
 def _check_bias(bias, N, device):
     if bias is None:
         return

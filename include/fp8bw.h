@@ -145,6 +145,23 @@ int fp8_tensorwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x
                          int64_t ld_q, float* recip, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fp8_tensorwise_quant_noalloc -- fp8_tensorwise_quant without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The partial amaxes go to a 4 KiB array the library holds on every GPU it
+ * runs on until the process ends (at most 1024 partials, enough for any
+ * input, so no size is refused for scratch; FP8BW_ERR_WORKSPACE guards the
+ * invariant).  The call allocates nothing; its first call on a device looks
+ * up that device's copy of the array (the device current at the call).
+ * Results are bit-identical to fp8_tensorwise_quant.  All calls on one GPU
+ * share the array: calls that overlap in time on one GPU (different
+ * streams) race and give undefined results; calls ordered on one stream are
+ * safe.  Arguments, layout and errors otherwise as fp8_tensorwise_quant.
+ */
+int fp8_tensorwise_quant_noalloc(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                 void* q, int64_t ld_q, float* recip, void* stream);
+
+/*
  * fp8_scaled_gemm_blockwise -- out[M, N] = sum_kb ra[m, kb] * rb[beta(n), kb]
  *                              * sum_{k in block kb} a[m, k] * b[n, k]
  * ([REPRO] What Changed: the blockwise GEMM on the same codes and

@@ -182,6 +182,11 @@ def test_tensorwise_validation(lib):
     assert q(P, 16, 32, 32, P, 32, P, P, 0, None) == WS
     assert q(P, 16, 30, 32, P, 32, P, P, 4096, None) == SHAPE
     assert lib.fp8bw_tensorwise_quant_ws_bytes(16, 32) >= 4
+    n = lib.fp8_tensorwise_quant_noalloc
+    assert n(P, 16, 30, 32, P, 32, P, None) == SHAPE                         # cols % 16
+    assert n(P, 16, 32, 32, P, 32, None, None) == NULL
+    assert n(P, 16, 32, 32, P + 1, 32, P, None) == ALIGN
+    assert n(P, 16, 32, 24, P, 32, P, None) == LAYOUT                        # ld_x < cols
 
 
 def test_linear_validation_and_workspace(lib):
