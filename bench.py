@@ -21,9 +21,12 @@ every launch give each kernel's average duration over the timed steps.
 
 Prints one JSON line: `value` is the step's effective throughput,
 3 * 2MNK flops / step time (TFLOP/s); `roofline` is for the dominant kernel,
-the forward blockwise GEMM (2MNK flops per launch / its average duration vs
-the 5.0 PFLOP/s dense FP8 peak); `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.  Also reported:
+the GEMM call with the largest share of the step's time (2MNK flops per call
+/ its average duration between HIP events on the launch stream, vs the 5.0
+PFLOP/s dense FP8 peak; a call is its main launch plus, where the plan has
+one, the split of the leftover tiles and their reduce); `rooflines` gives the
+same for every GEMM call of the step; `cpu_baseline` times the CPU oracle on
+a bounded sample of the same workload.  Also reported:
   separate_quant_step   the same step with the six separate quantizer
                         launches of fp8_linear_fwd / _dgrad / _wgrad (X and
                         dY each read twice);
@@ -32,7 +35,16 @@ bounded sample of the same workload.  Also reported:
   grouped_gemm          the mixture-of-experts grouped GEMM at the forward
                         shape;
   quant_standalone      the quantizers alone on S x S inputs, S = 1024 ..
-                        32768 (headline entries at 32768^2).
+                        32768 (headline entries at 32768^2);
+  tiny_linear           the 128 x 256 x 512 linear step (latency-bound);
+  per_tensor            per-tensor quantization of X [256, 1024] and
+                        W [4096, 1024] and the tensorwise GEMM, plus the
+                        16 x 32 x 32 fp32-out edge case;
+  tensorwise_quant      the per-tensor quantizer on large inputs (two passes:
+                        5 B moved per element, 3 B algorithmic);
+  long_k                the blockwise GEMM at M = N = 1024,
+                        K = 128000 / 128128 / 128256 (K split over the chip,
+                        then an ordered reduce).
 """
 
 import argparse
@@ -300,6 +312,186 @@ def grouped_gemm(seed, wl, groups=8, reps=10):
             "avg_us": round(ms * 1e3, 1), "tflops": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)}
 
 
+def _event_avg_ms(call, reps, warm=3):
+    """Average duration (ms) of `call` over `reps` back-to-back calls on
+    torch's current stream (the stream the library launches on), from one
+    HIP event pair around the whole run."""
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _graph_avg_ms(call, reps):
+    """The same calls captured once as a HIP graph and replayed (the host's
+    per-call cost drops out)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _gemm_entry(ms, flop):
+    t = flop / (ms * 1e-3) / 1e12
+    return {"avg_us": round(ms * 1e3, 2), "tflops": round(t, 2),
+            "frac_of_fp8_peak": round(t / FP8_PEAK_TFLOPS, 4)}
+
+
+def _quant_entry(ms, nbytes):
+    g = nbytes / (ms * 1e-3) / 1e9
+    return {"avg_us": round(ms * 1e3, 2), "gbps": round(g, 1),
+            "frac_of_hbm_peak": round(g / HBM_PEAK_GBS, 4)}
+
+
+def tiny_linear(seed, reps=200):
+    """The tiny linear: X [128, 512] N(0,1), W [256, 512] nn.Linear init, dY
+    [128, 256]; the fused training step (quantization included) and its
+    forward GEMM alone, eager and replayed from a HIP graph.  Latency-bound:
+    2MNK = 3.4e7 flops per GEMM."""
+    import blockwise_scaled_fp8_amd as fp8
+    dev = torch.device("cuda", 0)
+    shape = (128, 256, 512)
+    wl = Workload(seed, dev, shape)
+    plan = step_plan_dual(wl)
+    m, n, k = shape
+
+    def step():
+        for _, fn, _, _ in plan:
+            fn()
+    gemm = lambda: fp8.fp8_scaled_gemm_blockwise(wl.xq, wl.xr, wl.wq, wl.wr, "128x128", out=wl.y)  # noqa: E731
+    step()
+    ms = _event_avg_ms(step, reps)
+    gms = _graph_avg_ms(step, reps)
+    flop = 3 * 2 * m * n * k
+    return {"M": m, "N": n, "K": k, "plan": fp8.gemm_plan(m, n, k),
+            "step": {"launches": len(plan), "avg_us": round(ms * 1e3, 2),
+                     "graph_avg_us": round(gms * 1e3, 2),
+                     "graph_tflops": round(flop / (gms * 1e-3) / 1e12, 3)},
+            "gemm_fwd": dict(_gemm_entry(_event_avg_ms(gemm, reps), 2 * m * n * k),
+                             graph_avg_us=round(_graph_avg_ms(gemm, reps) * 1e3, 2))}
+
+
+def per_tensor(seed, reps=200):
+    """Per-tensor FP8: X [256, 1024] and W [4096, 1024] N(0,1) bf16, each
+    quantized with one scale (two launches: partial amax, then quantize;
+    5 B moved per element, 3 B algorithmic), and the tensorwise GEMM
+    256 x 4096 x 1024 with bf16 out; the 16 x 32 x 32 fp32-out edge case the
+    same way.  Both are latency-bound; graph-replayed times leave out the
+    host's per-call cost."""
+    import blockwise_scaled_fp8_amd as fp8
+    from synth import inputs
+    dev = torch.device("cuda", 0)
+    out = {}
+    for (m, n, k), od in (((256, 4096, 1024), torch.bfloat16), ((16, 32, 32), torch.float32)):
+        x = inputs.randn_bf16((m, k), seed=inputs.tensor_seed(seed + 30, "x"), device=dev)
+        w = inputs.randn_bf16((n, k), seed=inputs.tensor_seed(seed + 30, "w"), device=dev)
+        xq, xr = fp8.fp8_tensorwise_quant(x)
+        wq, wr = fp8.fp8_tensorwise_quant(w)
+        y = torch.empty(m, n, dtype=od, device=dev)
+        qx = lambda: fp8.fp8_tensorwise_quant(x, q=xq, recip=xr)  # noqa: E731
+        qw = lambda: fp8.fp8_tensorwise_quant(w, q=wq, recip=wr)  # noqa: E731
+        g = lambda: fp8.fp8_scaled_gemm_tensorwise(xq, xr, wq, wr, out=y)  # noqa: E731
+        e = {}
+        for name, fn, elems in (("quant X", qx, m * k), ("quant W", qw, n * k)):
+            ms, gms = _event_avg_ms(fn, reps), _graph_avg_ms(fn, reps)
+            e[name] = {"avg_us": round(ms * 1e3, 2), "graph_avg_us": round(gms * 1e3, 2),
+                       "graph_gbps_moved_5B": round(5 * elems / (gms * 1e-3) / 1e9, 1),
+                       "graph_gbps_algorithmic_3B": round(3 * elems / (gms * 1e-3) / 1e9, 1)}
+        e["gemm"] = dict(_gemm_entry(_event_avg_ms(g, reps), 2 * m * n * k),
+                         graph_avg_us=round(_graph_avg_ms(g, reps) * 1e3, 2))
+        e["gemm"]["graph_tflops"] = round(2 * m * n * k / (e["gemm"]["graph_avg_us"] * 1e-6) / 1e12, 2)
+        e["out"] = "bf16" if od == torch.bfloat16 else "fp32"
+        out[f"{m}x{n}x{k}"] = e
+    return out
+
+
+def tensorwise_quant_large(seed, sizes=(8192, 16384, 32768), reps=5):
+    """The per-tensor quantizer on S x S bf16 (inputs rotated over at least
+    1 GiB like the blockwise sweep): one amax pass (2 B read per element)
+    and one quantize pass (2 B read + 1 B written), so 5 B move per element
+    against 3 B algorithmic; both rates reported."""
+    import blockwise_scaled_fp8_amd as fp8
+    from synth import inputs
+    dev = torch.device("cuda", 0)
+    res = {}
+    for size in sizes:
+        nbuf = max(1, cdiv(1 << 30, 2 * size * size))
+        x0 = inputs.randn_bf16((size, size), seed=inputs.tensor_seed(seed, "a"), device=dev)
+        xs = [x0] + [x0.clone() for _ in range(nbuf - 1)]
+        qs = [torch.empty(size, size, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        rs = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(nbuf)]
+        calls = max(reps, 2 * nbuf)
+        it = {"i": 0}
+
+        def call():
+            i = it["i"] % nbuf
+            it["i"] += 1
+            fp8.fp8_tensorwise_quant(xs[i], q=qs[i], recip=rs[i])
+        ms = _event_avg_ms(call, calls)
+        e = size * size
+        res[str(size)] = {"buffers": nbuf, "avg_us": round(ms * 1e3, 2),
+                          "gbps_moved_5B": round(5 * e / (ms * 1e-3) / 1e9, 1),
+                          "frac_of_hbm_peak_moved": round(5 * e / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "gbps_algorithmic_3B": round(3 * e / (ms * 1e-3) / 1e9, 1),
+                          "frac_of_hbm_peak_algorithmic": round(3 * e / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del xs, qs, rs, x0
+        torch.cuda.empty_cache()
+    return res
+
+
+def long_k(seed, reps=10):
+    """The long-K blockwise GEMM: M = N = 1024, K = 128000 / 128128 / 128256
+    (1000 / 1001 / 1002 K blocks); A N(0,1) 1x128, B nn.Linear init
+    128x128, bf16 out.  The whole call (split-K main launch plus the ordered
+    reduce) per 2MNK flops; the quantizers of A and B are timed too."""
+    import blockwise_scaled_fp8_amd as fp8
+    from synth import inputs
+    dev = torch.device("cuda", 0)
+    m = n = 1024
+    res = {}
+    for k in (128000, 128128, 128256):
+        a = inputs.randn_bf16((m, k), seed=inputs.tensor_seed(seed + 20, "a"), device=dev)
+        b = inputs.linear_weight_bf16(n, k, seed=inputs.tensor_seed(seed + 20, "b"), device=dev)
+        aq, ar = fp8.fp8_blockwise_quant(a, "1x128")
+        bq, br = fp8.fp8_blockwise_quant(b, "128x128")
+        y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        ms = _event_avg_ms(lambda: fp8.fp8_scaled_gemm_blockwise(aq, ar, bq, br, "128x128", out=y), reps)
+        qa = _event_avg_ms(lambda: fp8.fp8_blockwise_quant(a, "1x128", q=aq, recip=ar), reps)
+        qb = _event_avg_ms(lambda: fp8.fp8_blockwise_quant(b, "128x128", q=bq, recip=br), reps)
+        res[str(k)] = {"k_blocks": k // 128, "plan": fp8.gemm_plan(m, n, k),
+                       "gemm": _gemm_entry(ms, 2 * m * n * k),
+                       "quant_1x128 A": _quant_entry(qa, quant_bytes(m, k, "1x128")),
+                       "quant_128x128 B": _quant_entry(qb, quant_bytes(n, k, "128x128"))}
+        del a, b, aq, bq, y
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(seed, min_seconds=10.0, max_samples=8):
     """The oracle, as it stands, on a bounded sample of the same workload.
     One sample: fwd and dgrad on 64 output rows (each with the full quantized
@@ -341,12 +533,13 @@ def cpu_baseline(seed, min_seconds=10.0, max_samples=8):
                        f"each operand used): {flops / 1e9:.1f} GFLOP in {total_t:.1f} s")}
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_fwd_blockwise_M16640_N5120_K8192_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "linear_step_M16640_N5120_K8192_traffic.md")
 GEMM_SOURCE = os.path.join(ROOT, "blockwise_scaled_fp8_amd", "csrc", "gemm.hip")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the forward GEMM, from the committed rocprofv3
+def measured_traffic(call):
+    """HBM bytes of one GEMM call of the step ("gemm fwd" / "gemm dgrad" /
+    "gemm wgrad", all its launches), from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary, valid only while the GEMM source is the
     one those counters were taken on (sha256 recorded in the summary)."""
     import hashlib
@@ -358,7 +551,29 @@ def measured_traffic():
         return None
     if rec.get("gemm_source_sha256") != sha:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_call", {}).get(call)
+
+
+def gemm_plans(shape=(M, N, K)):
+    """The launches of each GEMM call of the step (main launch, then the
+    leftover tiles' K split and reduce where the plan has them), from the
+    library's plan for this device."""
+    import blockwise_scaled_fp8_amd as fp8
+    m, n, k = shape
+    out = {}
+    for nm, (gm, gn, gk, mode) in (("gemm fwd", (m, n, k, "128x128")),
+                                   ("gemm dgrad", (m, k, n, "128x128")),
+                                   ("gemm wgrad", (n, k, m, "1x128"))):
+        pl = fp8.gemm_plan(gm, gn, gk, mode)
+        parts = [f"main launch {pl['tiles_full'] if pl['tail_splits'] > 1 else pl['tiles']} tiles"]
+        if pl["splits"] > 1:
+            parts[0] += f" x {pl['splits']} K splits"
+            parts.append("ordered reduce")
+        if pl["tail_splits"] > 1:
+            parts.append(f"{pl['tiles'] - pl['tiles_full']} leftover tiles x {pl['tail_splits']} K splits")
+            parts.append("ordered reduce")
+        out[nm] = dict(pl, launches=" + ".join(parts))
+    return out
 
 
 def copy_probe(gib):
@@ -403,8 +618,18 @@ def main():
     flops = 3 * 2 * M * N * K
     value = flops / (step_ms * 1e-3) / 1e12
     names = [p[0] for p in r["plan"]]
-    fwd_ms = r["per_ms"][names.index("gemm fwd")]
-    achieved = 2 * M * N * K / (fwd_ms * 1e-3) / 1e12
+    rooflines = {}
+    for nm in ("gemm fwd", "gemm dgrad", "gemm wgrad"):
+        ms = r["per_ms"][names.index(nm)]
+        ach = 2 * M * N * K / (ms * 1e-3) / 1e12
+        rooflines[nm] = {"bound": "mfma", "avg_us": round(ms * 1e3, 2),
+                         "flop_per_call": 2 * M * N * K, "achieved": round(ach, 1),
+                         "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / FP8_PEAK_TFLOPS, 4),
+                         "share_of_step": round(ms / r["gpu_ms_per_step"], 4)}
+    dominant = max(rooflines, key=lambda k: rooflines[k]["avg_us"])
+    dom = rooflines[dominant]
+    plans = gemm_plans()
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -423,9 +648,11 @@ def main():
                    "quantization": "fused: each bf16 tensor read once into both code layouts",
                    "seed": args.seed},
         "roofline": {"bound": "mfma",
-                     "kernel": "fwd blockwise GEMM call M16640 N5120 K8192 (main + tail-split + reduce launches)",
-                     "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": measured_traffic()},
+                     "kernel": f"{dominant.split()[1]} blockwise GEMM call "
+                               f"({plans[dominant]['launches']})",
+                     "achieved": dom["achieved"], "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": dom["frac"], "traffic": measured_traffic(dominant)},
+        "rooflines": {k: dict(v, launches=plans[k]["launches"]) for k, v in rooflines.items()},
         "gemm_tflops": {k: v["tflops"] for k, v in r["kernels"].items() if "tflops" in v},
         "quant_gbps": round(r["quant_gbps"], 1),
         "quant_frac_of_hbm_peak": round(r["quant_gbps"] / HBM_PEAK_GBS, 4),
@@ -461,6 +688,11 @@ def main():
         del r2
     if not args.no_quant_standalone:
         out["quant_standalone"] = quant_standalone(args.seed)
+    if not args.step_only:
+        out["tiny_linear"] = tiny_linear(args.seed)
+        out["per_tensor"] = per_tensor(args.seed)
+        out["tensorwise_quant"] = tensorwise_quant_large(args.seed)
+        out["long_k"] = long_k(args.seed)
     if args.copy_probe_gib > 0:
         out["copy_probe_bytes"] = copy_probe(args.copy_probe_gib)
     if not args.no_cpu_baseline:

@@ -22,6 +22,7 @@ from .ops import (  # noqa: F401
     fp8_tensorwise_quant,
     fp8_tensorwise_quant_noalloc,
     fp8bw_gemm_num_configs,
+    gemm_plan,
     linear_saved_bytes,
     linear_workspace,
     scale_grid,

@@ -282,17 +282,43 @@ FP8BW_API size_t fp8bw_gemm_blockwise_ws_bytes(int64_t M, int64_t N, int64_t K) 
   // chosen for a call also depends on its leading dimensions).
   fp8bw::GemmProblem p = {};
   p.M = M; p.N = N; p.K = K; p.lda = K; p.ldb = K;
-  p.mode = fp8bw::kBlockB128;
   size_t need = 0;
-  for (int c = 0; c < fp8bw::gemm_num_configs(); ++c) {
-    if (!fp8bw::gemm_config_ok(p, c)) continue;
-    const size_t b = fp8bw::gemm_plan(p, c, 0, true).ws_bytes;
-    if (b > need) need = b;
+  for (int mode : {fp8bw::kBlockB128, fp8bw::kBlockB1x128}) {
+    p.mode = mode;
+    for (int c = 0; c < fp8bw::gemm_num_configs(); ++c) {
+      if (!fp8bw::gemm_config_ok(p, c)) continue;
+      const size_t b = fp8bw::gemm_plan(p, c, 0, true).ws_bytes;
+      if (b > need) need = b;
+    }
   }
   return need;
 }
 
 FP8BW_API int fp8bw_gemm_num_configs(void) { return fp8bw::gemm_num_configs(); }
+
+FP8BW_API int fp8bw_gemm_blockwise_plan(int64_t M, int64_t N, int64_t K, int b_block,
+                                        int64_t* info) {
+  if (!info) return fail(FP8BW_ERR_NULL, "info must be non-null");
+  if (b_block != FP8BW_BLOCK_1x128 && b_block != FP8BW_BLOCK_128x128)
+    return fail(FP8BW_ERR_UNSUPPORTED, "unknown b_block %d", b_block);
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim || K % 128)
+    return fail(FP8BW_ERR_SHAPE, "plan needs 0 < M, N, K <= 2^30 and K %% 128 == 0");
+  // The plan of a call with contiguous operands, column-major scales and the
+  // workspace fp8bw_gemm_blockwise_ws_bytes(M, N, K) gives.
+  fp8bw::GemmProblem p = {};
+  p.M = M; p.N = N; p.K = K; p.lda = K; p.ldb = K;
+  p.ra_s_row = 1; p.ra_s_kb = M;
+  p.rb_s_row = 1; p.rb_s_kb = b_block == FP8BW_BLOCK_1x128 ? N : cdiv(N, 128);
+  p.mode = b_block == FP8BW_BLOCK_128x128 ? fp8bw::kBlockB128 : fp8bw::kBlockB1x128;
+  const fp8bw::GemmPlan pl = fp8bw::gemm_plan(p, -1, 0, true);
+  info[0] = pl.cfg;
+  info[1] = pl.splits;
+  info[2] = pl.tail_splits;
+  info[3] = pl.tiles;
+  info[4] = pl.tiles_full;
+  info[5] = (int64_t)pl.ws_bytes;
+  return ok();
+}
 
 FP8BW_API size_t fp8bw_gemm_ws_bytes_for_split(int64_t M, int64_t N, int splits) {
   if (M <= 0 || N <= 0 || splits <= 1) return 0;

@@ -960,30 +960,45 @@ static int num_cus() {
   return n;
 }
 
-static int heuristic_config(const GemmProblem& p) {
-  const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (p.M >= 256 && p.N >= 256 && t256 >= 128 && gemm_config_ok(p, 3)) return 3;
-  if (p.M >= 256 && p.N >= 128 && gemm_config_ok(p, 2)) return 2;
-  if (p.M >= 128 && p.N >= 128) return 0;
+// Built-in tile configuration: the largest tiles that still give the chip
+// at least half a round of workgroups, counting K splits where the call may
+// split (each piece at least 8 K blocks).  Measured: M = N = 1024 with 1000
+// K blocks runs 167 us on 256x256 tiles x 16 splits against 267 us on
+// 256x128 x 16; the 256 x 4096 x 1024 per-tensor GEMM 10.4 us on 64x64
+// tiles against 14.4 us on 256x128.
+static int heuristic_config(const GemmProblem& p, bool allow_split, int cus) {
+  auto tiles = [&](int bm, int bn) { return ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
+  const int64_t kblocks = (p.K + 127) / 128;
+  const int64_t half = cus / 2;
+  auto fills = [&](int bm, int bn) {
+    const int64_t t = tiles(bm, bn);
+    return t >= half || (allow_split && t * (kblocks / 8) >= cus);
+  };
+  if (gemm_config_ok(p, 3) && fills(256, 256)) return 3;
+  if (gemm_config_ok(p, 2) && fills(256, 128)) return 2;
+  if (p.M >= 128 && p.N >= 128 && fills(128, 128)) return 0;
   return 1;
 }
 
 GemmPlan gemm_plan(const GemmProblem& p, int config, int splits, bool allow_split) {
   GemmPlan pl;
-  pl.cfg = config >= 0 ? config : heuristic_config(p);
+  const int cus = num_cus();
+  pl.cfg = config >= 0 ? config : heuristic_config(p, allow_split && splits == 0, cus);
   const int bm = kCfgs[pl.cfg].bm, bn = kCfgs[pl.cfg].bn;
   const int64_t kblocks = (p.K + 127) / 128;
   pl.tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
   pl.splits = 1;
   pl.tail_splits = 1;
   pl.tiles_full = pl.tiles;
-  const int cus = num_cus();
   if (splits > 0) {
     pl.splits = splits;
   } else if (allow_split) {
     if (pl.tiles < cus && kblocks >= 16) {
-      // Too few tiles to fill the chip: split K over the whole problem.
-      int64_t want = (2 * cus + pl.tiles - 1) / pl.tiles;
+      // Too few tiles to fill the chip: split K over the whole problem, one
+      // round of pieces (a large-tile workgroup fills its CU's LDS; the
+      // small-tile kernel runs two workgroups per CU).
+      const int64_t slots = kCfgs[pl.cfg].kind == 1 ? cus : 2 * cus;
+      int64_t want = (slots + pl.tiles - 1) / pl.tiles;
       int64_t maxs = kblocks / 8;
       int64_t sp = want < maxs ? want : maxs;
       if (sp < 1) sp = 1;

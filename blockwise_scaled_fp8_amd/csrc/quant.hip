@@ -281,7 +281,23 @@ hipError_t launch_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t 
 // ---------------------------------------------------------------------------
 // Per-tensor: a grid of partial amaxes, then a quantize pass in which every
 // workgroup reduces the partials itself (fixed order, no atomics, no
-// memset) before quantizing its grid-stride share.
+// memset) before quantizing its grid-stride share.  Both passes stream: a
+// workgroup takes 16 KB blocks of 1024 consecutive 16-byte chunks in a grid
+// stride, each thread holding four independent nontemporal loads in flight
+// (one per 4 KB quarter of the block); the chunks past the last whole block
+// go one per thread.  A contiguous input is indexed linearly, a strided one
+// by row.
+constexpr int kTwUnroll = 4;
+constexpr int kTwBlock = 256 * kTwUnroll;   // chunks per workgroup block
+
+// Address of 16-byte chunk c (8 bf16 values) of a rows x cols input.
+__device__ __forceinline__ const uint16_t* tw_chunk(const uint16_t* x, int64_t c, int64_t cpr,
+                                                    int64_t ld_x, bool contiguous) {
+  if (contiguous) return x + c * 8;
+  const int64_t r = c / cpr;
+  return x + r * ld_x + (c - r * cpr) * 8;
+}
+
 __global__ __launch_bounds__(256) void amax_partial_kernel(const uint16_t* __restrict__ x,
                                                            int64_t rows, int64_t cols,
                                                            int64_t ld_x, float* __restrict__ ws) {
@@ -289,11 +305,18 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const uint16_t* __res
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t cpr = cols >> 3;
   const int64_t total = rows * cpr;
+  const bool contiguous = ld_x == cols;
+  const int64_t whole = total / kTwBlock * kTwBlock;
   float m = 0.f;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + tid; c < total; c += (int64_t)gridDim.x * 256) {
-    const int64_t r = c / cpr, k = c - r * cpr;
-    m = fmaxf(m, absmax8(*(const uint4*)(x + r * ld_x + k * 8)));
+  for (int64_t b = (int64_t)blockIdx.x * kTwBlock + tid; b < whole; b += (int64_t)gridDim.x * kTwBlock) {
+    uint4 v[kTwUnroll];
+#pragma unroll
+    for (int u = 0; u < kTwUnroll; ++u) v[u] = load_stream16(tw_chunk(x, b + 256 * u, cpr, ld_x, contiguous));
+#pragma unroll
+    for (int u = 0; u < kTwUnroll; ++u) m = fmaxf(m, absmax8(v[u]));
   }
+  for (int64_t c = whole + (int64_t)blockIdx.x * 256 + tid; c < total; c += (int64_t)gridDim.x * 256)
+    m = fmaxf(m, absmax8(load_stream16(tw_chunk(x, c, cpr, ld_x, contiguous))));
   m = wave_max(m);
   if (lane == 0) red[wave] = m;
   __syncthreads();
@@ -316,10 +339,22 @@ __global__ __launch_bounds__(256) void quant_tensorwise_kernel(
   if (blockIdx.x == 0 && tid == 0) *recip = recip_of_scale(s);
   const int64_t cpr = cols >> 3;
   const int64_t total = rows * cpr;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + tid; c < total; c += (int64_t)gridDim.x * 256) {
-    const int64_t r = c / cpr, k = c - r * cpr;
-    *(uint2*)(q + r * ld_q + k * 8) = quant8(*(const uint4*)(x + r * ld_x + k * 8), s);
+  const bool contiguous = ld_x == cols && ld_q == cols;
+  const int64_t whole = total / kTwBlock * kTwBlock;
+  auto qptr = [&](int64_t c) -> uint2* {
+    if (contiguous) return (uint2*)(q + c * 8);
+    const int64_t r = c / cpr;
+    return (uint2*)(q + r * ld_q + (c - r * cpr) * 8);
+  };
+  for (int64_t b = (int64_t)blockIdx.x * kTwBlock + tid; b < whole; b += (int64_t)gridDim.x * kTwBlock) {
+    uint4 v[kTwUnroll];
+#pragma unroll
+    for (int u = 0; u < kTwUnroll; ++u) v[u] = load_stream16(tw_chunk(x, b + 256 * u, cpr, ld_x, contiguous));
+#pragma unroll
+    for (int u = 0; u < kTwUnroll; ++u) *qptr(b + 256 * u) = quant8(v[u], s);
   }
+  for (int64_t c = whole + (int64_t)blockIdx.x * 256 + tid; c < total; c += (int64_t)gridDim.x * 256)
+    *qptr(c) = quant8(load_stream16(tw_chunk(x, c, cpr, ld_x, contiguous)), s);
 }
 
 int tensorwise_partials(int64_t rows, int64_t cols) {

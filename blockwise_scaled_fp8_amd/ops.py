@@ -275,6 +275,18 @@ def fp8bw_gemm_num_configs():
     return load_library().fp8bw_gemm_num_configs()
 
 
+def gemm_plan(M, N, K, b_block="128x128"):
+    """How the library runs an M x N x K blockwise GEMM (contiguous operands,
+    column-major scales) on the current device: tile configuration,
+    whole-problem split count, leftover-tile split count, tiles, tiles run
+    unsplit and workspace bytes."""
+    import ctypes
+    info = (ctypes.c_int64 * 6)()
+    check(load_library().fp8bw_gemm_blockwise_plan(M, N, K, BLOCKS[b_block], info))
+    keys = ("config", "splits", "tail_splits", "tiles", "tiles_full", "ws_bytes")
+    return dict(zip(keys, (int(v) for v in info)))
+
+
 @_on_tensor_device
 def fp8_scaled_gemm_tensorwise(a, ra, b, rb, out_dtype=torch.bfloat16, out=None, bias=None):
     """out[M, N] = (A . B^T) * ra * rb with one-element device scales."""

@@ -202,6 +202,17 @@ int fp8_scaled_gemm_blockwise(const void* a, int64_t lda, const float* ra, int64
  * split s is fp8bw_gemm_ws_bytes_for_split(M, N, s).
  */
 int fp8bw_gemm_num_configs(void);
+
+/*
+ * fp8bw_gemm_blockwise_plan -- how fp8_scaled_gemm_blockwise runs an
+ * M x N x K problem with contiguous operands and column-major scales on
+ * the current device (host query, launches nothing; for profiling and
+ * reporting).  Fills info[6] (caller-owned host array): tile
+ * configuration, whole-problem split-K count, split count of the leftover
+ * tiles of a partial last round, total tiles, tiles run unsplit, workspace
+ * bytes.  Requires 0 < M, N, K and K % 128 == 0.
+ */
+int fp8bw_gemm_blockwise_plan(int64_t M, int64_t N, int64_t K, int b_block, int64_t* info);
 size_t fp8bw_gemm_ws_bytes_for_split(int64_t M, int64_t N, int splits);
 int fp8_scaled_gemm_blockwise_cfg(const void* a, int64_t lda, const float* ra, int64_t ra_s_row,
                                   int64_t ra_s_kb, const void* b, int64_t ldb, const float* rb,

@@ -175,6 +175,26 @@ def test_quant_tensorwise(gpu, shape):
     assert_f32_equal(host_f32(r)[0], orc, f"tensorwise {shape}")
 
 
+@pytest.mark.parametrize("shape,ldx,ldq", [((1000, 208), 208, 208), ((300, 1024), 1040, 1056),
+                                           ((4099, 512), 520, 512)])
+def test_quant_tensorwise_strides_and_partial_blocks(gpu, shape, ldx, ldq):
+    """Per-tensor quantization of strided views (input row stride ldx, codes
+    written into a canary-filled [rows, ldq] buffer) and of chunk counts
+    that leave a partial 16 KB block after the whole ones."""
+    rows, cols = shape
+    xb = inputs.randn_bf16((rows, ldx), seed=inputs.tensor_seed(8, "x"))
+    x = xb[:, :cols]
+    buf = torch.full((rows, ldq), 0xA5, dtype=torch.uint8, device=gpu)
+    r = torch.empty(1, dtype=torch.float32, device=gpu)
+    say("quant tensorwise strided", shape, ldx, ldq)
+    fp8.fp8_tensorwise_quant(xb.to(gpu)[:, :cols], q=buf[:, :cols], recip=r)
+    torch.cuda.synchronize()
+    oq, orc = quant.quant_tensorwise(bits(x.contiguous()))
+    assert_codes_equal(host_u8(buf[:, :cols]), oq, f"tensorwise strided {shape}")
+    assert_f32_equal(host_f32(r)[0], orc, f"tensorwise strided {shape}")
+    assert bool((buf[:, cols:] == 0xA5).all())
+
+
 def test_quant_outputs_stay_in_bounds_and_honour_strides(gpu):
     """Canary-padded outputs: codes written with ld_q > cols, scales written
     row-major into a NaN-filled buffer with padding; nothing outside the
