@@ -332,7 +332,8 @@ __device__ __forceinline__ void stage_sync() {
 }
 
 // Tile order: XCD-aware (the dispatcher deals workgroups round-robin to the
-// 8 XCDs; xcd_remap gives each XCD a contiguous range of tile ids) then
+// 8 XCDs in linear workgroup order; xcd_remap gives each XCD a contiguous
+// range of ids) then
 // grouped (tile_to_mn: GROUP_M row-blocks per column sweep) so that
 // concurrently running tiles on one XCD share A and B slices in that XCD's
 // L2.
@@ -550,7 +551,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   int tm, tn;
   GemmArgs p = p_in;
-  const int tile_local = xcd_remap(blockIdx.x, gridDim.x);
+  // Workgroup -> (K split, tile): the whole grid, split-major, dealt out
+  // XCD-contiguously, so the workgroups an XCD runs together mostly share
+  // one K range and read the same A and B slices through its L2 (with the
+  // tiles of a split spread over XCDs, a long-K split-K GEMM streamed
+  // nearly every operand byte from the fabric).
+  const int nwg = gridDim.x * gridDim.y;
+  const int wg = xcd_remap(blockIdx.y * gridDim.x + blockIdx.x, nwg);
+  const int split = wg / gridDim.x;
+  const int tile_local = wg - split * gridDim.x;
   // Output tile [m0, m0 + BM) x [n0, n0 + BN).  The operand window the tile
   // loads, [ml, ml + BM) x [nl, nl + BN), is the same except at a ragged
   // edge, where it moves back to end exactly at the last row of A (of B):
@@ -570,7 +579,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int nl = min(n0, p.N - BN);
-  const int kb_begin = blockIdx.y * p.kb_per_split;
+  const int kb_begin = split * p.kb_per_split;
   const int kb_end = min(p.kblocks, kb_begin + p.kb_per_split);
 
   // Per-lane byte offsets of this wave's first row octets of A and B.  Lane
@@ -787,12 +796,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   int pm0 = 0, pn0 = 0;
   if constexpr (SPLIT) {
     if (p.part_tiled) {
-      pbase = p.partial + ((int64_t)blockIdx.y * gridDim.x + tile_local) * (BM * BN);
+      pbase = p.partial + ((int64_t)split * gridDim.x + tile_local) * (BM * BN);
       pld = BN;
       pm0 = m0;
       pn0 = n0;
     } else {
-      pbase = p.partial + (int64_t)blockIdx.y * p.M * p.N;
+      pbase = p.partial + (int64_t)split * p.M * p.N;
       pld = p.N;
     }
   }
@@ -805,7 +814,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
 }
 #undef FP8BW_ISSUE
 
-// Sum the split partials in split order and convert.
+// Sum the split partials [split][M][N] in split order and convert.  With
+// N % 4 == 0 a thread takes four consecutive columns (16-byte partial loads,
+// one 8- or 16-byte store where the output row allows it); otherwise one
+// element.  The sums are the same either way.
 template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int splits, int M, int N,
@@ -813,6 +825,42 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             int64_t ldo,
                                                             const uint16_t* __restrict__ bias) {
   const int64_t total = (int64_t)M * N;
+  if ((N & 3) == 0 && ((size_t)part & 15) == 0) {
+    const bool vec = (ldo & 3) == 0 && ((size_t)out & 15) == 0;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total / 4;
+         q += (int64_t)gridDim.x * 256) {
+      float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < splits; ++k) {
+        const float4 v = *(const float4*)(part + (int64_t)k * total + 4 * q);
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+      }
+      const int64_t m = 4 * q / N, n = 4 * q - m * N;
+      float val[4] = {s.x + bias_at(bias, (int)n), s.y + bias_at(bias, (int)n + 1),
+                      s.z + bias_at(bias, (int)n + 2), s.w + bias_at(bias, (int)n + 3)};
+      if (vec) {
+        if (OUT == kOutBf16) {
+          uint2 w;
+          w.x = f32_to_bf16_rne(val[0]) | (f32_to_bf16_rne(val[1]) << 16);
+          w.y = f32_to_bf16_rne(val[2]) | (f32_to_bf16_rne(val[3]) << 16);
+          *(uint2*)((uint16_t*)out + m * ldo + n) = w;
+        } else {
+          *(float4*)((float*)out + m * ldo + n) = make_float4(val[0], val[1], val[2], val[3]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (OUT == kOutBf16)
+            ((uint16_t*)out)[m * ldo + n + v] = (uint16_t)f32_to_bf16_rne(val[v]);
+          else
+            ((float*)out)[m * ldo + n + v] = val[v];
+        }
+      }
+    }
+    return;
+  }
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * 256) {
     float s = 0.f;
