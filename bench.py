@@ -217,8 +217,15 @@ def _time_quant(xs, qs, recips, block, reps, graph=False):
     per-call cost (Python, argument checks) drops out of the figure."""
     import blockwise_scaled_fp8_amd as fp8
     n = len(xs)
-    for i in range(min(n, 3)):
-        fp8.fp8_blockwise_quant(xs[i], block, q=qs[i], recip=recips[i])
+    # Warm-up of at least ~100 ms of calls: right after a single warm-up call
+    # a 32768^2 quantizer measured 8% slower than once the clock has settled.
+    t0 = time.perf_counter()
+    i = 0
+    while i < max(3, n) or time.perf_counter() - t0 < 0.1:
+        fp8.fp8_blockwise_quant(xs[i % n], block, q=qs[i % n], recip=recips[i % n])
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     calls = max(reps, 2 * n)
 
@@ -252,7 +259,7 @@ def _time_quant(xs, qs, recips, block, reps, graph=False):
     return e0.elapsed_time(e1) / calls
 
 
-def quant_standalone(seed, sizes=(1024, 2048, 4096, 8192, 16384, 32768), reps=10,
+def quant_standalone(seed, sizes=(1024, 2048, 4096, 8192, 16384, 32768), reps=20,
                      rotate_bytes=1 << 30):
     """The quantizers alone on square S x S bf16 inputs, both block shapes.
     Each size cycles through enough input / output buffer sets that their
