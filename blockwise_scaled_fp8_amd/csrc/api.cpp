@@ -46,14 +46,45 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int64_t kMaxDim = (int64_t)1 << 30;   // int32 indexing inside the kernels
 constexpr int64_t kMaxGridY = 65535;
 
+// Every element offset a call can form stays below 2^48: no allocation is
+// larger, and the bound keeps each product the host and the kernels form on
+// offsets (tile and byte offsets) far from int64 overflow.
+constexpr int64_t kMaxExtent = (int64_t)1 << 48;
+
+// (rows - 1) * ld + cols < kMaxExtent for a [rows, cols] matrix with
+// leading dimension ld (1 <= rows, cols <= 2^32; the product is not formed).
+bool extent_ok(int64_t rows, int64_t ld, int64_t cols) {
+  if (ld < 0) return false;
+  if (rows <= 1) return cols < kMaxExtent;
+  return cols < kMaxExtent && ld <= (kMaxExtent - 1 - cols) / (rows - 1);
+}
+
 // A strided 2-D scale grid [ni, nj] with strides (si, sj) must map distinct
-// index pairs to distinct addresses.
+// index pairs to distinct addresses, and its last element must lie below
+// kMaxExtent.  The stride of a dimension of size 1 is never used.
 bool strides_injective(int64_t ni, int64_t nj, int64_t si, int64_t sj) {
   if (si < 0 || sj < 0) return false;
   if (ni <= 1 && nj <= 1) return true;
-  if (ni <= 1) return sj >= 1;
-  if (nj <= 1) return si >= 1;
-  return (si >= 1 && sj >= si * ni) || (sj >= 1 && si >= sj * nj);
+  if (ni <= 1) return sj >= 1 && extent_ok(nj, sj, 1);
+  if (nj <= 1) return si >= 1 && extent_ok(ni, si, 1);
+  // sj >= si * ni (or si >= sj * nj) without forming the product
+  const bool nested = (si >= 1 && sj / ni >= si) || (sj >= 1 && si / nj >= sj);
+  if (!nested) return false;
+  // (ni - 1) * si + (nj - 1) * sj < kMaxExtent
+  if (!extent_ok(ni, si, 1)) return false;
+  const int64_t rest = kMaxExtent - 1 - (ni - 1) * si;
+  return sj <= rest / (nj - 1);
+}
+
+// The stride of a size-1 dimension is never used; pass 0 for it so that
+// no later arithmetic sees an arbitrary value.
+int64_t used_stride(int64_t n, int64_t s) { return n > 1 ? s : 0; }
+
+// a * b * c in size_t, SIZE_MAX when it does not fit.
+size_t mul_sat(size_t a, size_t b, size_t c) {
+  size_t ab, abc;
+  if (__builtin_mul_overflow(a, b, &ab) || __builtin_mul_overflow(ab, c, &abc)) return SIZE_MAX;
+  return abc;
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -82,7 +113,7 @@ FP8BW_API const char* fp8bw_last_error(void) { return g_err.c_str(); }
 // Quantization.
 
 static int check_quant_common(const void* x, int64_t rows, int64_t cols, int64_t ld_x, void* q,
-                              int64_t ld_q, int64_t q_row_len) {
+                              int64_t ld_q, int64_t q_rows, int64_t q_row_len) {
   if (rows < 0 || cols < 0) return fail(FP8BW_ERR_SHAPE, "negative rows/cols (%lld, %lld)",
                                         (long long)rows, (long long)cols);
   if (rows > kMaxDim * 4 || cols > kMaxDim) return fail(FP8BW_ERR_SHAPE, "dimension too large");
@@ -93,6 +124,8 @@ static int check_quant_common(const void* x, int64_t rows, int64_t cols, int64_t
   if (ld_x < cols || ld_x % 8) return fail(FP8BW_ERR_LAYOUT, "ld_x=%lld must be >= cols and a multiple of 8", (long long)ld_x);
   if (ld_q < q_row_len || ld_q % 16)
     return fail(FP8BW_ERR_LAYOUT, "ld_q=%lld must be >= %lld and a multiple of 16", (long long)ld_q, (long long)q_row_len);
+  if (!extent_ok(rows, ld_x, cols) || !extent_ok(q_rows, ld_q, q_row_len))
+    return fail(FP8BW_ERR_LAYOUT, "ld_x=%lld / ld_q=%lld reach past 2^48 elements", (long long)ld_x, (long long)ld_q);
   return FP8BW_OK;
 }
 
@@ -105,7 +138,7 @@ static int check_quant_output(const void* x, int64_t rows, int64_t cols, int64_t
     return fail(FP8BW_ERR_UNSUPPORTED, "unknown block kind %d", block);
   if (transpose != 0 && transpose != 1) return fail(FP8BW_ERR_UNSUPPORTED, "transpose must be 0 or 1");
   if (transpose && rows % 16) return fail(FP8BW_ERR_SHAPE, "transpose=1 needs rows %% 16 == 0 (rows=%lld)", (long long)rows);
-  int st = check_quant_common(x, rows, cols, ld_x, q, ld_q, transpose ? rows : cols);
+  int st = check_quant_common(x, rows, cols, ld_x, q, ld_q, transpose ? cols : rows, transpose ? rows : cols);
   if (st != FP8BW_OK) return st;
   if (rows == 0 || cols == 0) return FP8BW_OK;
   if (!recip) return fail(FP8BW_ERR_NULL, "recip must be non-null");
@@ -166,13 +199,15 @@ FP8BW_API int fp8_blockwise_quant_dual(const void* x, int64_t rows, int64_t cols
 
 FP8BW_API size_t fp8bw_tensorwise_quant_ws_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0) return 256;
+  if (rows > kMaxDim * 4 || cols > kMaxDim)   // rejected by the quantizer; the cap
+    return align_up((size_t)fp8bw::kMaxTensorwisePartials * sizeof(float));
   return align_up((size_t)fp8bw::tensorwise_partials(rows, cols) * sizeof(float));
 }
 
 FP8BW_API int fp8_tensorwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
                                    void* q, int64_t ld_q, float* recip, void* ws,
                                    size_t ws_bytes, void* stream) {
-  int st = check_quant_common(x, rows, cols, ld_x, q, ld_q, cols);
+  int st = check_quant_common(x, rows, cols, ld_x, q, ld_q, rows, cols);
   if (st != FP8BW_OK) return st;
   if (!recip) return fail(FP8BW_ERR_NULL, "recip must be non-null");
   if (!aligned(recip, 4)) return fail(FP8BW_ERR_ALIGN, "recip must be 4-byte aligned");
@@ -189,7 +224,7 @@ FP8BW_API int fp8_tensorwise_quant(const void* x, int64_t rows, int64_t cols, in
 FP8BW_API int fp8_tensorwise_quant_noalloc(const void* x, int64_t rows, int64_t cols,
                                            int64_t ld_x, void* q, int64_t ld_q, float* recip,
                                            void* stream) {
-  int st = check_quant_common(x, rows, cols, ld_x, q, ld_q, cols);
+  int st = check_quant_common(x, rows, cols, ld_x, q, ld_q, rows, cols);
   if (st != FP8BW_OK) return st;
   if (!recip) return fail(FP8BW_ERR_NULL, "recip must be non-null");
   if (!aligned(recip, 4)) return fail(FP8BW_ERR_ALIGN, "recip must be 4-byte aligned");
@@ -223,6 +258,9 @@ static int check_gemm_operands(const void* a, int64_t lda, const void* b, int64_
   if (lda < K || ldb < K || lda % 16 || ldb % 16)
     return fail(FP8BW_ERR_LAYOUT, "lda/ldb (%lld/%lld) must be >= K and multiples of 16", (long long)lda, (long long)ldb);
   if (ldo < N) return fail(FP8BW_ERR_LAYOUT, "ldo=%lld must be >= N", (long long)ldo);
+  if (!extent_ok(M, lda, K) || !extent_ok(N, ldb, K) || !extent_ok(M, ldo, N))
+    return fail(FP8BW_ERR_LAYOUT, "lda/ldb/ldo (%lld/%lld/%lld) reach past 2^48 elements",
+                (long long)lda, (long long)ldb, (long long)ldo);
   return FP8BW_OK;
 }
 
@@ -250,10 +288,11 @@ static int gemm_blockwise_impl(const void* a, int64_t lda, const float* ra, int6
     if (!strides_injective(nrb, kb, rb_s_row, rb_s_kb))
       return fail(FP8BW_ERR_LAYOUT, "rb strides (%lld, %lld) alias or are negative", (long long)rb_s_row, (long long)rb_s_kb);
   }
+  const int64_t nrb = b_block == FP8BW_BLOCK_1x128 ? N : cdiv(N, 128);
   fp8bw::GemmProblem p;
   p.a = a; p.lda = lda; p.b = b; p.ldb = ldb;
-  p.ra = ra; p.ra_s_row = ra_s_row; p.ra_s_kb = ra_s_kb;
-  p.rb = rb; p.rb_s_row = rb_s_row; p.rb_s_kb = rb_s_kb;
+  p.ra = ra; p.ra_s_row = used_stride(M, ra_s_row); p.ra_s_kb = used_stride(kb, ra_s_kb);
+  p.rb = rb; p.rb_s_row = used_stride(nrb, rb_s_row); p.rb_s_kb = used_stride(kb, rb_s_kb);
   p.out = out; p.ldo = ldo; p.M = M; p.N = N; p.K = K;
   p.mode = b_block == FP8BW_BLOCK_128x128 ? fp8bw::kBlockB128 : fp8bw::kBlockB1x128;
   p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
@@ -277,7 +316,7 @@ static int gemm_blockwise_impl(const void* a, int64_t lda, const float* ra, int6
 }
 
 FP8BW_API size_t fp8bw_gemm_blockwise_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   // Upper bound over every configuration's built-in plan (the configuration
   // chosen for a call also depends on its leading dimensions).
   fp8bw::GemmProblem p = {};
@@ -322,7 +361,7 @@ FP8BW_API int fp8bw_gemm_blockwise_plan(int64_t M, int64_t N, int64_t K, int b_b
 
 FP8BW_API size_t fp8bw_gemm_ws_bytes_for_split(int64_t M, int64_t N, int splits) {
   if (M <= 0 || N <= 0 || splits <= 1) return 0;
-  return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+  return mul_sat((size_t)splits, mul_sat((size_t)M, (size_t)N, 1), sizeof(float));
 }
 
 FP8BW_API int fp8_scaled_gemm_blockwise(const void* a, int64_t lda, const float* ra,
@@ -380,22 +419,31 @@ FP8BW_API int fp8_scaled_grouped_gemm_blockwise(
   if (!group_end) return fail(FP8BW_ERR_NULL, "group_end must be non-null");
   if (!aligned(group_end, 4)) return fail(FP8BW_ERR_ALIGN, "group_end must be 4-byte aligned");
   const int64_t kb = K / 128, nb = cdiv(N, 128);
-  if (b_s_group < (N - 1) * ldb + K || b_s_group % 16)
+  // B groups: each group's [N, K] block lies inside its stride, and the
+  // last group's end below 2^48 elements.
+  const int64_t b_extent = (N - 1) * ldb + K;
+  if (b_s_group < b_extent || b_s_group % 16)
     return fail(FP8BW_ERR_LAYOUT, "b_s_group=%lld must be >= (N-1)*ldb + K and a multiple of 16", (long long)b_s_group);
+  if (groups > 1 && b_s_group > (kMaxExtent - b_extent) / (groups - 1))
+    return fail(FP8BW_ERR_LAYOUT, "b_s_group=%lld: %d groups reach past 2^48 elements", (long long)b_s_group, groups);
   if (kb > 0) {
     if (!ra || !rb) return fail(FP8BW_ERR_NULL, "ra and rb must be non-null");
     if (!aligned(ra, 4) || !aligned(rb, 4)) return fail(FP8BW_ERR_ALIGN, "ra/rb must be 4-byte aligned");
     if (kb > 1 && ra_s_kb < M) return fail(FP8BW_ERR_LAYOUT, "ra must be column-major: ra_s_kb >= M");
+    if (!strides_injective(M, kb, 1, ra_s_kb))
+      return fail(FP8BW_ERR_LAYOUT, "ra_s_kb=%lld reaches past 2^48 elements", (long long)ra_s_kb);
     if (!strides_injective(nb, kb, rb_s_row, rb_s_kb))
       return fail(FP8BW_ERR_LAYOUT, "rb strides (%lld, %lld) alias or are negative", (long long)rb_s_row, (long long)rb_s_kb);
-    const int64_t rb_extent = (nb - 1) * rb_s_row + (kb - 1) * rb_s_kb + 1;
+    const int64_t rb_extent = (nb - 1) * used_stride(nb, rb_s_row) + (kb - 1) * used_stride(kb, rb_s_kb) + 1;
     if (groups > 1 && rb_s_group < rb_extent)
       return fail(FP8BW_ERR_LAYOUT, "rb_s_group=%lld overlaps a group's %lld scales", (long long)rb_s_group, (long long)rb_extent);
+    if (groups > 1 && rb_s_group > (kMaxExtent - rb_extent) / (groups - 1))
+      return fail(FP8BW_ERR_LAYOUT, "rb_s_group=%lld: %d groups reach past 2^48 elements", (long long)rb_s_group, groups);
   }
   fp8bw::GemmProblem p;
   p.a = a; p.lda = lda; p.b = b; p.ldb = ldb;
-  p.ra = ra; p.ra_s_row = 1; p.ra_s_kb = ra_s_kb;
-  p.rb = rb; p.rb_s_row = rb_s_row; p.rb_s_kb = rb_s_kb;
+  p.ra = ra; p.ra_s_row = 1; p.ra_s_kb = used_stride(kb, ra_s_kb);
+  p.rb = rb; p.rb_s_row = used_stride(nb, rb_s_row); p.rb_s_kb = used_stride(kb, rb_s_kb);
   p.out = out; p.ldo = ldo; p.M = M; p.N = N; p.K = K;
   p.mode = fp8bw::kBlockB128;
   p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
@@ -541,12 +589,13 @@ int check_linear(const void* p0, const void* p1, void* out, int64_t M, int64_t N
 
 FP8BW_API size_t fp8bw_linear_ws_bytes(int64_t M, int64_t N, int64_t K, int which) {
   if (which < 0 || which > 4 || M <= 0 || N <= 0 || K <= 0) return 0;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   if (which >= 3) return fused_layout(M, N, K, which).total;
   return linear_layout(M, N, K, which).total;
 }
 
 FP8BW_API size_t fp8bw_linear_saved_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   return saved_layout(M, N, K).total;
 }
 

@@ -974,12 +974,16 @@ bool gemm_config_ok(const GemmProblem& p, int cfg) {
     // 128x128 B scales: a wave's 64 columns must stay inside one scale
     // block when the last column tile moves back to end at row N - 1.
     if (p.mode == kBlockB128 && p.N % 64) return false;
-    const int64_t lim = (int64_t)1 << 31;
-    if (256 * p.lda + p.K >= lim || 256 * p.ldb + p.K >= lim) return false;
+    // n * stride + extra < 2^31, without forming the product
+    auto fits31 = [](int64_t n, int64_t stride, int64_t extra) {
+      const int64_t room = ((int64_t)1 << 31) - 1 - extra;
+      return stride >= 0 && room >= 0 && stride <= room / n;
+    };
+    if (!fits31(256, p.lda, p.K) || !fits31(256, p.ldb, p.K)) return false;
     if (p.mode != kTensorwise) {
-      if (256 * p.ra_s_row * 4 >= lim) return false;
+      if (!fits31(256 * 4, p.ra_s_row, 0)) return false;
       const int64_t rb_rows = p.mode == kBlockB128 ? (p.N + 127) / 128 : 256;
-      if (rb_rows * p.rb_s_row * 4 >= lim) return false;
+      if (!fits31(rb_rows * 4, p.rb_s_row, 0)) return false;
     }
   }
   return true;
@@ -1074,8 +1078,12 @@ GemmPlan gemm_plan(const GemmProblem& p, int config, int splits, bool allow_spli
       }
     }
   }
-  if (pl.splits > 1)
-    pl.ws_bytes = (size_t)pl.splits * (size_t)p.M * (size_t)p.N * sizeof(float);
+  size_t mn, part;
+  if (pl.splits > 1)   // SIZE_MAX when it does not fit (no workspace is that large)
+    pl.ws_bytes = __builtin_mul_overflow((size_t)p.M, (size_t)p.N, &mn) ||
+                          __builtin_mul_overflow(mn, (size_t)pl.splits * sizeof(float), &part)
+                      ? SIZE_MAX
+                      : part;
   else if (pl.tail_splits > 1)
     pl.ws_bytes = (size_t)pl.tail_splits * (size_t)(pl.tiles - pl.tiles_full) * bm * bn * sizeof(float);
   else

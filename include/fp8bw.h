@@ -32,7 +32,14 @@
  *    Every matrix pointer must be 16-byte aligned, bf16 input leading
  *    dimensions a multiple of 8 and FP8 leading dimensions a multiple of 16
  *    (GEMM output leading dimensions only need ldo >= N).  The stride of a
- *    dimension of size 1 is ignored.
+ *    dimension of size 1 is ignored.  Every element offset a call can form
+ *    ((rows - 1) * ld + cols of each matrix, the last scale of a strided
+ *    scale grid, the last group of a grouped operand) must be below 2^48;
+ *    larger ones give FP8BW_ERR_LAYOUT.
+ *  - Dimensions are at most 2^30 (quantizer rows 2^32).  The GEMM and
+ *    linear size queries return 0 for larger ones (the calls reject them),
+ *    and fp8bw_gemm_ws_bytes_for_split returns SIZE_MAX when the size does
+ *    not fit a size_t.
  *  - A *reciprocal scale* ("recip") is the dequantization multiplier: the
  *    quantizer computes s = 448 / max(amax, 1e-12) per block, stores
  *    codes = satRNE_e4m3(x * s) and recip = 1 / s (both fp32 IEEE ops),
