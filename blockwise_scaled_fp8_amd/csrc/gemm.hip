@@ -65,7 +65,36 @@ struct GemmArgs {
   int groups;
   const int* group_end;
   int64_t b_s_group, rb_s_group;
+  // Which rows of each group a grouped launch covers (group_part_rows).
+  int group_part;
 };
+
+// A grouped GEMM on the large tiles runs as two launches: the large-tile
+// kernel takes every group's whole 256-row tiles, and its last partial tile
+// too when that holds more than 128 rows (part 1); the 64x64 small-tile
+// kernel takes the remaining last partial tiles of at most 128 rows (part 2).
+// A group's last tile of a few rows then costs a few 64-row tiles instead of
+// a whole 256-row tile.  Part 0 is every row of every group in one launch.
+constexpr int kGroupBigRows = 256;
+constexpr int kGroupSmallRows = 128;
+
+// Rows [first, first + rows) of a group of mg rows that part `part` covers.
+__host__ __device__ __forceinline__ void group_part_rows(int part, int mg, int* first, int* rows) {
+  if (part == 0) {
+    *first = 0;
+    *rows = mg;
+    return;
+  }
+  const int full = mg / kGroupBigRows * kGroupBigRows, rem = mg - full;
+  const bool big = rem > kGroupSmallRows;
+  if (part == 1) {
+    *first = 0;
+    *rows = big ? mg : full;
+  } else {
+    *first = full;
+    *rows = big ? 0 : rem;
+  }
+}
 
 __device__ __forceinline__ float bias_at(const uint16_t* bias, int n) {
   return bias ? bf16lo(bias[n]) : 0.f;
@@ -472,25 +501,43 @@ __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM
   }
 }
 
+// Number of tiles of a grouped GEMM's group table (each group's row tiles
+// times the column tiles), with the same clamping as locate_group_tile.
+template <int BM>
+__device__ __forceinline__ int grouped_tile_count(const GemmArgs& p) {
+  int tiles = 0, row0 = 0;
+  for (int g = 0; g < p.groups; ++g) {
+    const int end = max(row0, min(p.group_end[g], p.M));
+    int first, rows;
+    group_part_rows(p.group_part, end - row0, &first, &rows);
+    tiles += (rows + BM - 1) / BM;
+    row0 = end;
+  }
+  return tiles * p.tiles_n;
+}
+
 // Grouped GEMM: find the group and tile of (remapped) tile id t, and point
-// p at that group's rows of A, ra and out and at its B and B scales.  Tiles
-// are numbered group by group (tiles_m(g) x tiles_n each, grouped order
-// inside a group).  Returns false for ids past the last tile (the grid is
-// sized for the worst case of every group's last row tile being partial).
+// p at the rows of that group this launch covers (group_part_rows) in A, ra
+// and out, and at its B and B scales.  Tiles are numbered group by group
+// (tiles_m(g) x tiles_n each, grouped order inside a group).  Returns false
+// for ids past the last tile (the grid is sized for the worst case of every
+// group's last row tile being partial).
 template <int BM, int OUT>
 __device__ __forceinline__ bool locate_group_tile(GemmArgs& p, int t, int* tm, int* tn, int* row0_out) {
   int start = 0, row0 = 0;
   for (int g = 0; g < p.groups; ++g) {
     const int end = max(row0, min(p.group_end[g], p.M));
-    const int mg = end - row0;
+    int first, mg;
+    group_part_rows(p.group_part, end - row0, &first, &mg);
     const int mt = (mg + BM - 1) / BM;
     const int nt = mt * p.tiles_n;
     if (t < start + nt) {
+      const int r0 = row0 + first;
       tile_to_mn(t - start, mt, p.tiles_n, tm, tn);
-      *row0_out = row0;
-      p.a += (int64_t)row0 * p.lda;
-      p.ra += (int64_t)row0 * p.ra_s_row;
-      p.out = (uint8_t*)p.out + (int64_t)row0 * p.ldo * (OUT == kOutBf16 ? 2 : 4);
+      *row0_out = r0;
+      p.a += (int64_t)r0 * p.lda;
+      p.ra += (int64_t)r0 * p.ra_s_row;
+      p.out = (uint8_t*)p.out + (int64_t)r0 * p.ldo * (OUT == kOutBf16 ? 2 : 4);
       p.b += (int64_t)g * p.b_s_group;
       p.rb += (int64_t)g * p.rb_s_group;
       p.M = mg;
@@ -556,8 +603,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   // one K range and read the same A and B slices through its L2 (with the
   // tiles of a split spread over XCDs, a long-K split-K GEMM streamed
   // nearly every operand byte from the fabric).
+  // A grouped GEMM's grid covers the worst case of its group table; its
+  // tiles are dealt out over the tiles that exist, so that the workgroups
+  // past them are the last of every XCD rather than a run on the last XCDs
+  // (which left the other XCDs a partly filled extra round).
   const int nwg = gridDim.x * gridDim.y;
-  const int wg = xcd_remap(blockIdx.y * gridDim.x + blockIdx.x, nwg);
+  int wg;
+  if (p.groups > 0) {
+    const int T = grouped_tile_count<BM>(p);
+    constexpr int kXcds = 8;
+    const int x = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+    const int full = T / kXcds, rem = T % kXcds;
+    if (q >= full + (x < rem ? 1 : 0)) return;
+    wg = x * full + min(x, rem) + q;
+  } else {
+    wg = xcd_remap(blockIdx.y * gridDim.x + blockIdx.x, nwg);
+  }
   const int split = wg / gridDim.x;
   const int tile_local = wg - split * gridDim.x;
   // Output tile [m0, m0 + BM) x [n0, n0 + BN).  The operand window the tile
@@ -1190,6 +1251,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
   a.part_tiled = 0;
   a.bias = (const uint16_t*)p.bias;
   a.groups = 0;
+  a.group_part = 0;
   a.group_end = nullptr;
   a.b_s_group = a.rb_s_group = 0;
   const int splits = pl.splits < 1 ? 1 : pl.splits;
@@ -1241,8 +1303,24 @@ static int grouped_config(const GemmProblem& p) {
   return (p.M >= 128 && p.N >= 128) ? 0 : 1;
 }
 
+// Groups up to this count run as the two launches of group_part_rows; more
+// run as one (each workgroup scans the group table, and the small-tile
+// launch's grid grows with the count).
+constexpr int kMaxSplitGroups = 64;
+
+static bool grouped_split(const GemmProblem& p, int groups) {
+  return kCfgs[grouped_config(p)].kind == 1 && groups <= kMaxSplitGroups;
+}
+
 bool grouped_gemm_ok(const GemmProblem& p, int groups) {
-  return groups > 0 && p.K % 128 == 0;
+  if (groups <= 0 || p.K % 128) return false;
+  // Grids: (row tiles + groups) x column tiles workgroups, in 31 bits.
+  const int cfg = grouped_config(p);
+  const int64_t grid = ((p.M + kCfgs[cfg].bm - 1) / kCfgs[cfg].bm + groups) *
+                       ((p.N + kCfgs[cfg].bn - 1) / kCfgs[cfg].bn);
+  const int64_t grid2 = grouped_split(p, groups) ? 2 * (int64_t)groups * ((p.N + 63) / 64) : 0;
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  return grid <= lim && grid2 <= lim;
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, int groups, const int* group_end,
@@ -1275,12 +1353,25 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, int groups, const int* grou
   a.rb_s_group = rb_s_group;
   const int64_t tiles_m = (p.M + bm - 1) / bm + groups;
   if (kCfgs[cfg].kind == 0) {
+    a.group_part = 0;
     a.tiles_m = (int)tiles_m;   // grid only; each tile's group sets its own
     return cfg == 0 ? launch_mode<128, 128>(a, p.mode, 1, p.out_kind, stream)
                     : launch_mode<64, 64>(a, p.mode, 1, p.out_kind, stream);
   }
+  static_assert(kGroupBigRows == 256 && kGroupSmallRows <= kGroupBigRows,
+                "part 1 runs on the 256-row large tiles");
+  const bool split = grouped_split(p, groups);
+  a.group_part = split ? 1 : 0;
   a.tiles_m = 0;
-  return launch_v2_cfg(cfg, a, p.mode, (int)(tiles_m * a.tiles_n), 1, p.out_kind, stream);
+  hipError_t e = launch_v2_cfg(cfg, a, p.mode, (int)(tiles_m * a.tiles_n), 1, p.out_kind, stream);
+  if (e != hipSuccess || !split) return e;
+  // Part 2: the groups' last partial tiles of at most 128 rows, at most two
+  // 64-row tiles per group.
+  GemmArgs s2 = a;
+  s2.group_part = 2;
+  s2.tiles_n = (int)((p.N + 63) / 64);
+  s2.tiles_m = 2 * groups;   // grid only
+  return launch_mode<64, 64>(s2, p.mode, 1, p.out_kind, stream);
 }
 
 }  // namespace fp8bw

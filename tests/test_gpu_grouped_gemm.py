@@ -90,6 +90,16 @@ def test_grouped_small_problems_use_the_small_tiles(gpu, mn):
     _case(gpu, 4, M, N, 512, ends, "f32", seed=56 + M)
 
 
+@pytest.mark.parametrize("od", ["bf16", "f32"])
+def test_grouped_last_tile_remainders(gpu, od):
+    """Groups whose last 256-row tile holds 1, 63, 64, 65, 128, 129 or 255
+    rows, or none: at most 128 rows go to the 64x64 second launch, more stay
+    on the large tiles; groups smaller than a tile, and an empty group."""
+    sizes = [256 + 1, 512 + 63, 64, 256 + 65, 128, 0, 256 + 129, 255, 512]
+    ends = np.cumsum(sizes)
+    _case(gpu, len(sizes), int(ends[-1]), 512, 256, list(ends), od, seed=57)
+
+
 def test_grouped_malformed_table_is_clamped(gpu):
     """Decreasing ends and ends past M are clamped to [previous end, M]."""
     _case(gpu, 4, 512, 256, 256, [200, 100, 9999, 50], "f32", seed=54)
