@@ -65,8 +65,11 @@ struct GemmArgs {
   int groups;
   const int* group_end;
   int64_t b_s_group, rb_s_group;
-  // Which rows of each group a grouped launch covers (group_part_rows).
+  // Which rows of each group a grouped launch covers (group_part_rows), and
+  // what grouped_split_pays weighs: the CUs one round of large tiles
+  // occupies and the large tiles' column width.
   int group_part;
+  int group_cus, group_big_bn;
 };
 
 // A grouped GEMM on the large tiles runs as two launches: the large-tile
@@ -94,6 +97,30 @@ __host__ __device__ __forceinline__ void group_part_rows(int part, int mg, int* 
     *first = full;
     *rows = big ? 0 : rem;
   }
+}
+
+// Whether the two-launch split of a grouped GEMM pays for this group table:
+// it does when the groups' last partial tiles of at most 128 rows, left on
+// the large tiles, would take one more round of the chip's CUs than the
+// large tiles take without them.  Otherwise they fit in the last round's
+// idle CUs, and the second launch, which reads each such group's B once
+// more, would only add time; both launches then run part 0 and nothing.
+// Every workgroup of both launches reaches the same answer from the same
+// table.
+__device__ __forceinline__ bool grouped_split_pays(const GemmArgs& p) {
+  int all = 0, big = 0, row0 = 0;
+  for (int g = 0; g < p.groups; ++g) {
+    const int end = max(row0, min(p.group_end[g], p.M));
+    int first, rows;
+    group_part_rows(1, end - row0, &first, &rows);
+    all += (end - row0 + kGroupBigRows - 1) / kGroupBigRows;
+    big += (rows + kGroupBigRows - 1) / kGroupBigRows;
+    row0 = end;
+  }
+  const int64_t tn = (p.N + p.group_big_bn - 1) / p.group_big_bn;
+  const int64_t rounds_all = ((int64_t)all * tn + p.group_cus - 1) / p.group_cus;
+  const int64_t rounds_big = ((int64_t)big * tn + p.group_cus - 1) / p.group_cus;
+  return rounds_big < rounds_all;
 }
 
 __device__ __forceinline__ float bias_at(const uint16_t* bias, int n) {
@@ -170,6 +197,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p_in) {
   int tm, tn;
   if (p.groups > 0) {
     // Grouped GEMM: p now addresses this tile's group (rows clamp to it).
+    if (p.group_part == 2 && !grouped_split_pays(p)) return;
     int row0;
     if (!locate_group_tile<BM, OUT>(p, blockIdx.x, &tm, &tn, &row0)) return;
   } else {
@@ -610,6 +638,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const int nwg = gridDim.x * gridDim.y;
   int wg;
   if (p.groups > 0) {
+    if (p.group_part == 1 && !grouped_split_pays(p)) p.group_part = 0;
     const int T = grouped_tile_count<BM>(p);
     constexpr int kXcds = 8;
     const int x = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
@@ -1252,6 +1281,8 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
   a.bias = (const uint16_t*)p.bias;
   a.groups = 0;
   a.group_part = 0;
+  a.group_cus = 1;
+  a.group_big_bn = bn;
   a.group_end = nullptr;
   a.b_s_group = a.rb_s_group = 0;
   const int splits = pl.splits < 1 ? 1 : pl.splits;
@@ -1354,6 +1385,8 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, int groups, const int* grou
   const int64_t tiles_m = (p.M + bm - 1) / bm + groups;
   if (kCfgs[cfg].kind == 0) {
     a.group_part = 0;
+    a.group_cus = 1;
+    a.group_big_bn = bn;
     a.tiles_m = (int)tiles_m;   // grid only; each tile's group sets its own
     return cfg == 0 ? launch_mode<128, 128>(a, p.mode, 1, p.out_kind, stream)
                     : launch_mode<64, 64>(a, p.mode, 1, p.out_kind, stream);
@@ -1362,6 +1395,8 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, int groups, const int* grou
                 "part 1 runs on the 256-row large tiles");
   const bool split = grouped_split(p, groups);
   a.group_part = split ? 1 : 0;
+  a.group_cus = num_cus();
+  a.group_big_bn = bn;
   a.tiles_m = 0;
   hipError_t e = launch_v2_cfg(cfg, a, p.mode, (int)(tiles_m * a.tiles_n), 1, p.out_kind, stream);
   if (e != hipSuccess || !split) return e;

@@ -100,6 +100,23 @@ def test_grouped_last_tile_remainders(gpu, od):
     _case(gpu, len(sizes), int(ends[-1]), 512, 256, list(ends), od, seed=57)
 
 
+def test_grouped_split_launch_when_it_saves_a_round(gpu):
+    """16 whole 256-row tiles x 16 column tiles fill one round of 256 CUs;
+    the groups' small last tiles (1, 64, 65, 128 and 10 rows) would need a
+    second round, so they run in the 64-row second launch (on MI355X's 256
+    CUs; with another count the same table may run in one launch, which the
+    check covers as well).  Sampled rows: every group's first and last rows
+    and random ones."""
+    sizes = [4 * 256 + 1, 4 * 256 + 64, 0, 4 * 256 + 65, 10, 4 * 256 + 128]
+    ends = np.cumsum(sizes)
+    M = int(ends[-1])
+    rng = np.random.default_rng(58)
+    starts = np.r_[0, ends[:-1]]
+    sample = np.unique(np.r_[starts[np.array(sizes) > 0], ends[np.array(sizes) > 0] - 1,
+                             ends[np.array(sizes) > 0] - 2, rng.integers(0, M, 24)])
+    _case(gpu, len(sizes), M, 4096, 256, list(ends), "bf16", seed=58, sample=sample)
+
+
 def test_grouped_malformed_table_is_clamped(gpu):
     """Decreasing ends and ends past M are clamped to [previous end, M]."""
     _case(gpu, 4, 512, 256, 256, [200, 100, 9999, 50], "f32", seed=54)
