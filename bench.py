@@ -625,6 +625,8 @@ def main():
                          "grouped GEMM or standalone quantizers (for profiling runs)")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--only", choices=["long_k"], default=None,
+                    help="run this one other workload alone and print its record (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the hot path runs "
@@ -635,6 +637,9 @@ def main():
         print("bench.py runs as a single process on one GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.only == "long_k":
+        print(json.dumps({"long_k": long_k(args.seed)}), flush=True)
+        return
     r = run_gpu(args.steps, args.warmup, args.seed, plan_fn=step_plan_dual)
     step_ms = r["gpu_ms_per_step"]
     flops = 3 * 2 * M * N * K
