@@ -304,7 +304,8 @@ def grouped_gemm(seed, wl, groups=8, reps=10):
     """The grouped (mixture-of-experts) blockwise GEMM at the forward shape:
     the M = 16640 quantized tokens of X split over `groups` experts with
     seeded multinomial sizes, one 128x128-quantized N x K weight per expert;
-    2MNK flops in total, timed with HIP events like the step."""
+    2MNK flops in total, timed with a HIP event pair around `reps` calls
+    after at least 0.5 s of warm-up calls."""
     import numpy as np
     import blockwise_scaled_fp8_amd as fp8
     from synth import inputs
@@ -319,28 +320,30 @@ def grouped_gemm(seed, wl, groups=8, reps=10):
     ends = torch.tensor(np.cumsum(sizes), dtype=torch.int32, device=dev)
     out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     call = lambda: fp8.fp8_scaled_grouped_gemm_blockwise(wl.xq, wl.xr, wq, wr, ends, out=out)  # noqa: E731
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    evs[0].record(stream)
-    for i in range(reps):
-        call()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(reps)) / reps
+    ms = _event_avg_ms(call, reps, warm_s=0.5)
+    tflops = 2 * M * N * K / (ms * 1e-3) / 1e12
     return {"groups": groups, "group_rows": [int(v) for v in sizes], "M": M, "N": N, "K": K,
-            "avg_us": round(ms * 1e3, 1), "tflops": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+            "avg_us": round(ms * 1e3, 1), "tflops": round(tflops, 1),
+            "frac_of_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+            "launches": "whole 256x256 row tiles of every expert (and last tiles of more than "
+                        "128 rows), then the experts' smaller last tiles as 64x64 tiles when that "
+                        "saves a round of the CUs"}
 
 
-def _event_avg_ms(call, reps, warm=3):
+def _event_avg_ms(call, reps, warm=3, warm_s=0.0):
     """Average duration (ms) of `call` over `reps` back-to-back calls on
     torch's current stream (the stream the library launches on), from one
-    HIP event pair around the whole run."""
+    HIP event pair around the whole run.  Warm-up: `warm` calls, then more
+    until `warm_s` seconds have passed (the shader clock settles at its
+    loaded level within a few hundred ms of sustained MFMA work)."""
     for _ in range(warm):
         call()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -502,7 +505,8 @@ def long_k(seed, reps=10):
         aq, ar = fp8.fp8_blockwise_quant(a, "1x128")
         bq, br = fp8.fp8_blockwise_quant(b, "128x128")
         y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-        ms = _event_avg_ms(lambda: fp8.fp8_scaled_gemm_blockwise(aq, ar, bq, br, "128x128", out=y), reps)
+        ms = _event_avg_ms(lambda: fp8.fp8_scaled_gemm_blockwise(aq, ar, bq, br, "128x128", out=y),
+                           reps, warm_s=0.3)
         qa = _event_avg_ms(lambda: fp8.fp8_blockwise_quant(a, "1x128", q=aq, recip=ar), reps)
         qb = _event_avg_ms(lambda: fp8.fp8_blockwise_quant(b, "128x128", q=bq, recip=br), reps)
         res[str(k)] = {"k_blocks": k // 128, "plan": fp8.gemm_plan(m, n, k),

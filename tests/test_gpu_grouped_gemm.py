@@ -100,7 +100,8 @@ def test_grouped_last_tile_remainders(gpu, od):
     _case(gpu, len(sizes), int(ends[-1]), 512, 256, list(ends), od, seed=57)
 
 
-def test_grouped_split_launch_when_it_saves_a_round(gpu):
+@pytest.mark.parametrize("od", ["bf16", "f32"])
+def test_grouped_split_launch_when_it_saves_a_round(gpu, od):
     """16 whole 256-row tiles x 16 column tiles fill one round of 256 CUs;
     the groups' small last tiles (1, 64, 65, 128 and 10 rows) would need a
     second round, so they run in the 64-row second launch (on MI355X's 256
@@ -114,7 +115,7 @@ def test_grouped_split_launch_when_it_saves_a_round(gpu):
     starts = np.r_[0, ends[:-1]]
     sample = np.unique(np.r_[starts[np.array(sizes) > 0], ends[np.array(sizes) > 0] - 1,
                              ends[np.array(sizes) > 0] - 2, rng.integers(0, M, 24)])
-    _case(gpu, len(sizes), M, 4096, 256, list(ends), "bf16", seed=58, sample=sample)
+    _case(gpu, len(sizes), M, 4096, 256, list(ends), od, seed=58, sample=sample)
 
 
 def test_grouped_malformed_table_is_clamped(gpu):
