@@ -118,6 +118,17 @@ def test_grouped_split_launch_when_it_saves_a_round(gpu, od):
     _case(gpu, len(sizes), M, 4096, 256, list(ends), od, seed=58, sample=sample)
 
 
+def test_grouped_many_groups_one_launch(gpu):
+    """More groups than the two-launch split takes (80 > 64): every row in
+    one large-tile launch, groups of 0 .. 120 rows."""
+    rng = np.random.default_rng(59)
+    sizes = rng.integers(0, 121, 80)
+    ends = np.cumsum(sizes)
+    M = int(ends[-1])
+    sample = np.unique(np.r_[ends[sizes > 0] - 1, rng.integers(0, M, 40)])
+    _case(gpu, 80, M, 512, 256, list(ends), "bf16", seed=59, sample=sample)
+
+
 def test_grouped_malformed_table_is_clamped(gpu):
     """Decreasing ends and ends past M are clamped to [previous end, M]."""
     _case(gpu, 4, 512, 256, 256, [200, 100, 9999, 50], "f32", seed=54)
