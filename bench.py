@@ -551,8 +551,17 @@ def cpu_baseline(seed, min_seconds=10.0, max_samples=8):
         total_t += time.perf_counter() - t0
         n += 1
     flops = flops_one * n
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(flops / total_t / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
+            "host": {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+                     "torch_threads": torch.get_num_threads(), "blas_threads": threads,
+                     "cpu_model": model},
             "sample": (f"{n} samples, each the oracle (quantize + block-rescaled float64 GEMM) "
                        f"for fwd and dgrad on {rows} of {M} output rows and wgrad on {rows} x "
                        f"{kcols} of {N} x {K} outputs (full contraction, full quantization of "
