@@ -268,7 +268,7 @@ int fp8_scaled_gemm_tensorwise_bias(const void* a, int64_t lda, const float* ra,
                                     void* stream);
 
 /*
- * fp8_scaled_grouped_gemm_blockwise -- one launch for G GEMMs that share N
+ * fp8_scaled_grouped_gemm_blockwise -- one call for G GEMMs that share N
  * and K and split the rows of A and out into consecutive groups, each with
  * its own B (the mixture-of-experts layout: tokens sorted by expert, one
  * weight per expert; the pages mention the grouped scaled matmul of MoE
@@ -291,7 +291,13 @@ int fp8_scaled_gemm_tensorwise_bias(const void* a, int64_t lda, const float* ra,
  *   rb_s_group  large enough that groups' scale grids do not overlap.
  *   Requires K % 128 == 0; no split-K, no workspace.  Problems with
  *   M >= 256 and N >= 128 (and 256*lda + K, 256*ldb + K < 2^31) run on the
- *   large-tile kernels, others on the small-tile kernel.
+ *   large-tile kernels, others on the small-tile kernel.  With up to 64
+ *   groups on the large tiles the call enqueues two launches: the second
+ *   takes the groups' last partial row tiles of at most 128 rows as 64-row
+ *   tiles when the table (read on the device) shows that this saves a round
+ *   of the GPU's compute units; otherwise it returns at once.  Every row is
+ *   written by exactly one launch.  The grids must fit in 2^31 - 1
+ *   workgroups (else FP8BW_ERR_UNSUPPORTED).
  */
 int fp8_scaled_grouped_gemm_blockwise(const void* a, int64_t lda, const float* ra,
                                       int64_t ra_s_kb, const void* b, int64_t ldb,
