@@ -17,6 +17,7 @@ from .ops import (  # noqa: F401
     fp8_linear_fwd_save,
     fp8_linear_wgrad,
     fp8_scaled_gemm_blockwise,
+    fp8_scaled_gemm_blockwise_kn,
     fp8_scaled_gemm_tensorwise,
     fp8_scaled_grouped_gemm_blockwise,
     fp8_tensorwise_quant,

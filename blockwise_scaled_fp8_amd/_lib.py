@@ -31,6 +31,9 @@ PROTOTYPES = {
     "fp8_scaled_gemm_blockwise": (c_int, [c_ptr, c_i64, c_ptr, c_i64, c_i64, c_ptr, c_i64, c_ptr,
                                           c_i64, c_i64, c_int, c_i64, c_i64, c_i64, c_ptr, c_i64,
                                           c_int, c_ptr, c_size, c_ptr]),
+    "fp8_scaled_gemm_blockwise_kn": (c_int, [c_ptr, c_i64, c_ptr, c_i64, c_i64, c_ptr, c_i64,
+                                             c_ptr, c_i64, c_i64, c_int, c_i64, c_i64, c_i64,
+                                             c_ptr, c_i64, c_int, c_ptr, c_size, c_ptr]),
     "fp8bw_gemm_num_configs": (c_int, []),
     "fp8bw_gemm_blockwise_plan": (c_int, [c_i64, c_i64, c_i64, c_int, c_ptr]),
     "fp8bw_gemm_ws_bytes_for_split": (c_size, [c_i64, c_i64, c_int]),

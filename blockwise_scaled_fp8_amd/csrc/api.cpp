@@ -245,7 +245,7 @@ FP8BW_API int fp8_tensorwise_quant_noalloc(const void* x, int64_t rows, int64_t 
 
 static int check_gemm_operands(const void* a, int64_t lda, const void* b, int64_t ldb,
                                int64_t M, int64_t N, int64_t K, void* out, int64_t ldo,
-                               int out_dtype) {
+                               int out_dtype, bool b_kn = false) {
   if (out_dtype != FP8BW_OUT_BF16 && out_dtype != FP8BW_OUT_F32)
     return fail(FP8BW_ERR_UNSUPPORTED, "unknown out_dtype %d", out_dtype);
   if (M < 0 || N < 0 || K < 0)
@@ -255,10 +255,12 @@ static int check_gemm_operands(const void* a, int64_t lda, const void* b, int64_
   if (!a || !b || !out) return fail(FP8BW_ERR_NULL, "a, b and out must be non-null");
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16))
     return fail(FP8BW_ERR_ALIGN, "a, b and out must be 16-byte aligned");
-  if (lda < K || ldb < K || lda % 16 || ldb % 16)
-    return fail(FP8BW_ERR_LAYOUT, "lda/ldb (%lld/%lld) must be >= K and multiples of 16", (long long)lda, (long long)ldb);
+  if (lda < K || ldb < (b_kn ? N : K) || lda % 16 || ldb % 16)
+    return fail(FP8BW_ERR_LAYOUT, "lda/ldb (%lld/%lld) must be >= K/%s and multiples of 16",
+                (long long)lda, (long long)ldb, b_kn ? "N" : "K");
   if (ldo < N) return fail(FP8BW_ERR_LAYOUT, "ldo=%lld must be >= N", (long long)ldo);
-  if (!extent_ok(M, lda, K) || !extent_ok(N, ldb, K) || !extent_ok(M, ldo, N))
+  if (!extent_ok(M, lda, K) || !(b_kn ? extent_ok(K, ldb, N) : extent_ok(N, ldb, K)) ||
+      !extent_ok(M, ldo, N))
     return fail(FP8BW_ERR_LAYOUT, "lda/ldb/ldo (%lld/%lld/%lld) reach past 2^48 elements",
                 (long long)lda, (long long)ldb, (long long)ldo);
   return FP8BW_OK;
@@ -269,10 +271,10 @@ static int gemm_blockwise_impl(const void* a, int64_t lda, const float* ra, int6
                                int64_t rb_s_row, int64_t rb_s_kb, int b_block, int64_t M,
                                int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype,
                                int config, int splits, void* ws, size_t ws_bytes, void* stream,
-                               const void* bias = nullptr) {
+                               const void* bias = nullptr, bool b_kn = false) {
   if (b_block != FP8BW_BLOCK_1x128 && b_block != FP8BW_BLOCK_128x128)
     return fail(FP8BW_ERR_UNSUPPORTED, "unknown b_block %d", b_block);
-  int st = check_gemm_operands(a, lda, b, ldb, M, N, K, out, ldo, out_dtype);
+  int st = check_gemm_operands(a, lda, b, ldb, M, N, K, out, ldo, out_dtype, b_kn);
   if (st != FP8BW_OK) return st;
   if (K % 128) return fail(FP8BW_ERR_SHAPE, "blockwise GEMM needs K %% 128 == 0 (K=%lld)", (long long)K);
   if (M == 0 || N == 0) return ok();
@@ -297,6 +299,11 @@ static int gemm_blockwise_impl(const void* a, int64_t lda, const float* ra, int6
   p.mode = b_block == FP8BW_BLOCK_128x128 ? fp8bw::kBlockB128 : fp8bw::kBlockB1x128;
   p.out_kind = out_dtype == FP8BW_OUT_BF16 ? fp8bw::kOutBf16 : fp8bw::kOutF32;
   p.bias = bias;
+  p.b_kn = b_kn ? 1 : 0;
+  if (b_kn && !fp8bw::gemm_config_ok(p, 3))
+    return fail(FP8BW_ERR_UNSUPPORTED,
+                "B in [K, N] layout needs M, N >= 256, N %% 16 == 0 (%% 64 with 128x128 B "
+                "scales) and 256 * ldb + K < 2^31");
   if (config >= 0 && !fp8bw::gemm_config_ok(p, config))
     return fail(FP8BW_ERR_UNSUPPORTED, "config %d does not support this problem", config);
   if (splits > kMaxGridY || (kb > 0 && splits > kb) || (kb == 0 && splits > 1))
@@ -386,6 +393,17 @@ FP8BW_API int fp8_scaled_gemm_blockwise_cfg(const void* a, int64_t lda, const fl
   if (splits < 0) return fail(FP8BW_ERR_SHAPE, "splits must be >= 0");
   return gemm_blockwise_impl(a, lda, ra, ra_s_row, ra_s_kb, b, ldb, rb, rb_s_row, rb_s_kb, b_block,
                              M, N, K, out, ldo, out_dtype, config, splits, ws, ws_bytes, stream);
+}
+
+FP8BW_API int fp8_scaled_gemm_blockwise_kn(const void* a, int64_t lda, const float* ra,
+                                           int64_t ra_s_row, int64_t ra_s_kb, const void* b_kn,
+                                           int64_t ldb, const float* rb, int64_t rb_s_row,
+                                           int64_t rb_s_kb, int b_block, int64_t M, int64_t N,
+                                           int64_t K, void* out, int64_t ldo, int out_dtype,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  return gemm_blockwise_impl(a, lda, ra, ra_s_row, ra_s_kb, b_kn, ldb, rb, rb_s_row, rb_s_kb,
+                             b_block, M, N, K, out, ldo, out_dtype, -1, 0, ws, ws_bytes, stream,
+                             nullptr, true);
 }
 
 static int check_bias(const void* bias) {

@@ -70,6 +70,9 @@ struct GemmArgs {
   // occupies and the large tiles' column width.
   int group_part;
   int group_cus, group_big_bn;
+  // B given in [K, N] layout (b[k * ldb + n], N contiguous) instead of
+  // [N, K]; large 256x256 tiles only.
+  int b_kn;
 };
 
 // A grouped GEMM on the large tiles runs as two launches: the large-tile
@@ -163,6 +166,27 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int row, int half)
 constexpr int kRowPrefetch = 1;
 // MFMA steps between a partial's MFMA and its rescale (ring of delay + 1).
 constexpr int kRingDelay = 2;
+
+// Fragment of a B tile stored in [K, N] layout (see gemm_v2_kernel): four
+// transposing 8-byte LDS reads (ds_read_b64_tr_b8) 8 rows apart.  Within
+// each 16-lane group, result byte b of lane i is byte i % 8 of the 8 bytes
+// that lane 2 b + i / 8 addresses, so lanes 2 b and 2 b + 1 point at row
+// r0 + b, columns c and c + 8, and lane i receives column c + i of rows
+// r0 .. r0 + 7: 8 consecutive K values of its output column.
+__device__ __forceinline__ v8i load_frag_kn(const uint8_t* tile, uint32_t off) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) v2i lds_v2i;
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  lds_u8* t = (lds_u8*)(uint8_t*)tile + off;
+  const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(t));
+  const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(t + 2048));
+  const v2i r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(t + 4096));
+  const v2i r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(t + 6144));
+  v8i f;
+  f[0] = r0.x; f[1] = r0.y; f[2] = r1.x; f[3] = r1.y;
+  f[4] = r2.x; f[5] = r2.y; f[6] = r3.x; f[7] = r3.y;
+  return f;
+}
 
 // Fragment read at precomputed byte offsets of its two 16-byte chunks.
 __device__ __forceinline__ v8i load_frag_at(const uint8_t* tile, uint32_t lo, uint32_t hi) {
@@ -430,11 +454,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // rb_voff are this lane's byte offsets of its scale slots (row times the
 // scale row stride), precomputed by the caller; ra_base / rb_base point at
 // the scales of the tile's first row (row block) in K block 0.
-template <int AI, int BI, int RAI, int RBI, int RAB, int RBB, int NW, int MODE>
+template <int AI, int BI, int RAI, int RBI, int RAB, int RBB, int NW, int MODE, bool BKN>
 __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* sa, uint8_t* sb,
                                             float* sra, float* srb, __amdgpu_buffer_rsrc_t ars,
                                             __amdgpu_buffer_rsrc_t brs, uint32_t a_voff,
-                                            uint32_t b_voff, const uint32_t (&ra_voff)[RAI > 0 ? RAI : 1],
+                                            uint32_t b_voff, uint32_t b_voff_hi,
+                                            const uint8_t* bkn_base, int bkn_cols,
+                                            const uint32_t (&ra_voff)[RAI > 0 ? RAI : 1],
                                             const uint32_t (&rb_voff)[RBI > 0 ? RBI : 1],
                                             const float* ra_base, int64_t ra_bytes,
                                             const float* rb_base, int64_t rb_bytes, int wave) {
@@ -444,10 +470,26 @@ __device__ __forceinline__ void issue_stage(const GemmArgs& p, int kb, uint8_t* 
   for (int i = 0; i < AI; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void_t*)(sa + (wave + NW * i) * 1024), 16,
                                              a_voff, ko + 8 * NW * i * (int)p.lda, 0, 0);
+  if constexpr (BKN) {
+    // B in [K, N] layout: the stage holds the K block's 128 rows of B, each
+    // of the tile's 256 columns (row-major, 256 bytes a row); load i fills
+    // rows 4 o .. 4 o + 3, o = wave + NW i.  The descriptor starts at the K
+    // block's first row, so every offset stays below 128 rows.
+    const __amdgpu_buffer_rsrc_t bk =
+        buffer_rsrc(bkn_base + (int64_t)ko * p.ldb, (int64_t)127 * p.ldb + bkn_cols);
 #pragma unroll
-  for (int i = 0; i < BI; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void_t*)(sb + (wave + NW * i) * 1024), 16,
-                                             b_voff, ko + 8 * NW * i * (int)p.ldb, 0, 0);
+    for (int i = 0; i < BI; ++i) {
+      const int o = wave + NW * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bk, (lds_void_t*)(sb + o * 1024), 16,
+                                               ((o >> 3) & 1) ? b_voff_hi : b_voff,
+                                               4 * o * (int)p.ldb, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void_t*)(sb + (wave + NW * i) * 1024), 16,
+                                               b_voff, ko + 8 * NW * i * (int)p.ldb, 0, 0);
+  }
   if constexpr (MODE != kTensorwise) {
     const __amdgpu_buffer_rsrc_t rars = buffer_rsrc(ra_base + (int64_t)kb * p.ra_s_kb, ra_bytes);
 #pragma unroll
@@ -578,7 +620,8 @@ __device__ __forceinline__ bool locate_group_tile(GemmArgs& p, int t, int* tm, i
   return false;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int MODE, int OUT, bool SPLIT>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int MODE, int OUT, bool SPLIT,
+          bool BKN = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs p_in) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -686,6 +729,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
       buffer_rsrc(p.a + (int64_t)ml * p.lda, (int64_t)BM * p.lda);
   const __amdgpu_buffer_rsrc_t brs =
       buffer_rsrc(p.b + (int64_t)nl * p.ldb, (int64_t)BN * p.ldb);
+  // B in [K, N] layout: row r of a K block's B tile (256 bytes, the tile's
+  // columns) is stored with 16-byte chunk c at c ^ swz_kn(r), swz_kn(r) =
+  // (r & 7) | (((r >> 5) & 1) << 3), so that each pass of a transposing
+  // fragment read (32 lanes: 16 rows, one chunk each) meets every bank once.
+  // Lane 16 q + c of a direct load fills physical chunk c of row 4 o + q;
+  // (4 o + q) & 7 = 4 (o & 1) + q with o & 1 == wave & 1, and bit 3 of the
+  // swizzle is bit 3 of o (two offsets).
+  static_assert(!BKN || (BN == 256 && LW % 2 == 0), "[K, N] B tiles are 256 columns wide");
+  uint32_t b_voff_hi = 0;
+  uint32_t bkn_voff = 0;
+  if constexpr (BKN) {
+    const int q = lane >> 4, c = lane & 15, f0 = 4 * (wave & 1) + q;
+    bkn_voff = (uint32_t)(q * p.ldb + 16 * (c ^ f0));
+    b_voff_hi = (uint32_t)(q * p.ldb + 16 * (c ^ (f0 | 8)));
+  }
   // Scale slots of this lane.  ra lands transposed per wave row band of 16 TM
   // rows, in groups of four sub-tiles: LDS slot k = 16 TM h + 64 q + 4 r + v
   // holds row 16 TM h + 16 (4 q + v) + r, so a lane (fragment row r) finds
@@ -718,9 +776,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
 
 #define FP8BW_ISSUE(kb, st)                                                                   \
   if (wave < LW)                                                                              \
-  issue_stage<AI, BI, RAI, RBI, RAB, RBB, LW, MODE>(p, (kb), sA[st], sB[st], sRa[st], sRb[st], \
-                                                    ars, brs, a_voff, b_voff, ra_voff, rb_voff, \
-                                                    ra_base, ra_bytes, rb_base, rb_bytes, wave)
+  issue_stage<AI, BI, RAI, RBI, RAB, RBB, LW, MODE, BKN>(                                     \
+      p, (kb), sA[st], sB[st], sRa[st], sRb[st], ars, brs, a_voff, BKN ? bkn_voff : b_voff,    \
+      b_voff_hi, p.b + nl, BN, ra_voff, rb_voff, ra_base, ra_bytes, rb_base, rb_bytes, wave)
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -765,6 +823,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     uint32_t ra_off = (wm0 + 4 * frow) * 4;
     uint32_t rb_off = (wn0 + 4 * fhalf) * 4;
     asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(ra_off), "+v"(rb_off));
+    // [K, N] B tiles: sub-tile j's transposing reads (see load_frag_kn) --
+    // lanes 2 b and 2 b + 1 of group g = fhalf address row 32 g + b (+ 8 per
+    // read), the two halves of the chunk holding columns wn0 + 16 j ..
+    uint32_t bkn[BKN ? TN : 1];
+    if constexpr (BKN) {
+      const int r = 32 * fhalf + (frow >> 1);
+      const int sw = (frow >> 1) | ((fhalf & 1) << 3);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        bkn[j] = (uint32_t)(r * 256 + 16 * (((wn0 >> 4) + j) ^ sw) + 8 * (frow & 1));
+        asm volatile("" : "+v"(bkn[j]));
+      }
+    }
+    auto load_b = [&](const uint8_t* tB_, int j) -> v8i {
+      if constexpr (BKN) return load_frag_kn(tB_, bkn[j]);
+      else return load_frag_at(tB_, b_lo + 2048 * j, b_hi + 2048 * j);
+    };
     const uint8_t* tA = sA[st];
     const uint8_t* tB = sB[st];
     const uint8_t* tRa = (const uint8_t*)sRa[st];
@@ -780,16 +855,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
       // complete in order, so the first MFMA waits for two fragments, not
       // for all of the K block's head (tensorwise +2%; with block scales,
       // whose products the head also computes, it measured slower).
-      bf[0] = load_frag_at(tB, b_lo, b_hi);
+      bf[0] = load_b(tB, 0);
       af[0] = load_frag_at(tA, a_lo, a_hi);
 #pragma unroll
-      for (int j = 1; j < TN; ++j) bf[j] = load_frag_at(tB, b_lo + 2048 * j, b_hi + 2048 * j);
+      for (int j = 1; j < TN; ++j) bf[j] = load_b(tB, j);
 #pragma unroll
       for (int i = 1; i < PF; ++i) af[i] = load_frag_at(tA, a_lo + 2048 * i, a_hi + 2048 * i);
       __builtin_amdgcn_sched_barrier(0);   // keep that order
     } else {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bf[j] = load_frag_at(tB, b_lo + 2048 * j, b_hi + 2048 * j);
+      for (int j = 0; j < TN; ++j) bf[j] = load_b(tB, j);
     }
     // Row scales of this lane's TM sub-tile rows (one row per sub-tile:
     // the partials are computed transposed, see below), times the 128x128
@@ -1053,6 +1128,12 @@ int gemm_num_configs() { return kNumCfgs; }
 
 bool gemm_config_ok(const GemmProblem& p, int cfg) {
   if (cfg < 0 || cfg >= kNumCfgs) return false;
+  if (p.b_kn) {
+    // B in [K, N] layout: 256x256 tiles only; 16-byte column chunks of B
+    // rows (N % 16), and the offsets of a K block's 128 rows in 31 bits.
+    if (cfg != 3 || p.K % 128 || p.M < 256 || p.N < 256 || p.N % 16) return false;
+    if (p.ldb < 0 || p.ldb > (((int64_t)1 << 31) - 1 - 256) / 128) return false;
+  }
   if (kCfgs[cfg].kind == 1) {
     // The large-tile kernels load whole 128-byte K blocks (no K tail), need
     // at least one whole tile in each dimension (an edge tile's operand
@@ -1109,6 +1190,7 @@ static int num_cus() {
 // 256x128 x 16; the 256 x 4096 x 1024 per-tensor GEMM 10.4 us on 64x64
 // tiles against 14.4 us on 256x128.
 static int heuristic_config(const GemmProblem& p, bool allow_split, int cus) {
+  if (p.b_kn) return 3;
   auto tiles = [&](int bm, int bn) { return ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
   const int64_t kblocks = (p.K + 127) / 128;
   const int64_t half = cus / 2;
@@ -1181,27 +1263,27 @@ GemmPlan gemm_plan(const GemmProblem& p, int config, int splits, bool allow_spli
   return pl;
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, int MODE>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int MODE, bool BKN = false>
 static hipError_t launch_v2(const GemmArgs& a, int ntiles, int splits, int out_kind,
                             hipStream_t stream) {
   dim3 grid((unsigned)ntiles, (unsigned)splits);
   dim3 block(64 * WGM * WGN);
   if (splits > 1)
-    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutF32, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutF32, true, BKN>), grid, block, 0, stream, a);
   else if (out_kind == kOutBf16)
-    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutBf16, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutBf16, false, BKN>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutF32, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutF32, false, BKN>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool BKN = false>
 static hipError_t launch_v2_mode(const GemmArgs& a, int mode, int ntiles, int splits,
                                  int out_kind, hipStream_t stream) {
   switch (mode) {
-    case kBlockB128: return launch_v2<BM, BN, WGM, WGN, STAGES, kBlockB128>(a, ntiles, splits, out_kind, stream);
-    case kBlockB1x128: return launch_v2<BM, BN, WGM, WGN, STAGES, kBlockB1x128>(a, ntiles, splits, out_kind, stream);
-    default: return launch_v2<BM, BN, WGM, WGN, STAGES, kTensorwise>(a, ntiles, splits, out_kind, stream);
+    case kBlockB128: return launch_v2<BM, BN, WGM, WGN, STAGES, kBlockB128, BKN>(a, ntiles, splits, out_kind, stream);
+    case kBlockB1x128: return launch_v2<BM, BN, WGM, WGN, STAGES, kBlockB1x128, BKN>(a, ntiles, splits, out_kind, stream);
+    default: return launch_v2<BM, BN, WGM, WGN, STAGES, kTensorwise, BKN>(a, ntiles, splits, out_kind, stream);
   }
 }
 
@@ -1226,6 +1308,7 @@ static hipError_t launch_tiled_reduce(const GemmArgs& a, int splits, int ntiles,
 // One launch of large-tile config `cfg` over grouped tiles [base, base + ntiles).
 static hipError_t launch_v2_cfg(int cfg, const GemmArgs& a, int mode, int ntiles, int splits,
                                 int out_kind, hipStream_t stream) {
+  if (a.b_kn) return launch_v2_mode<256, 256, 2, 4, 2, true>(a, mode, ntiles, splits, out_kind, stream);
   if (cfg == 2) return launch_v2_mode<256, 128, 2, 2, 3>(a, mode, ntiles, splits, out_kind, stream);
   return launch_v2_mode<256, 256, 2, 4, 2>(a, mode, ntiles, splits, out_kind, stream);
 }
@@ -1279,6 +1362,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
   a.tile_base = 0;
   a.part_tiled = 0;
   a.bias = (const uint16_t*)p.bias;
+  a.b_kn = p.b_kn;
   a.groups = 0;
   a.group_part = 0;
   a.group_cus = 1;

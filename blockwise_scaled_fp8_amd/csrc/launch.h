@@ -60,6 +60,7 @@ struct GemmProblem {
   int mode;       // ScaleMode
   int out_kind;   // OutKind
   const void* bias = nullptr;   // optional bf16 [N] added before the output cast
+  int b_kn = 0;                 // B given as [K, N] (b[k * ldb + n]) instead of [N, K]
 };
 
 // Tile configurations; the table lives in gemm.hip.

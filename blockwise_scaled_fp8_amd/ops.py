@@ -271,6 +271,41 @@ def fp8_scaled_gemm_blockwise(a, ra, b, rb, b_block="128x128", out_dtype=torch.b
     return out
 
 
+@_on_tensor_device
+def fp8_scaled_gemm_blockwise_kn(a, ra, b_kn, rb, b_block="128x128", out_dtype=torch.bfloat16,
+                                 out=None):
+    """out[M, N] = blockwise-scaled A . B with B given in [K, N] layout
+    (N contiguous), e.g. a weight's codes W [N_w, K_w] used as the B of
+    dX = dY . W without a transposed copy (see include/fp8bw.h).
+
+    a uint8 [M, K], ra fp32 [M, K/128], b_kn uint8 [K, N], rb fp32
+    [N/128 or N, K/128] indexed by (output column block, K block)."""
+    lib = load_library()
+    _need_cuda(a, b_kn, ra, rb)
+    _rowmajor(a, "a")
+    _rowmajor(b_kn, "b_kn")
+    M, K = a.shape
+    if b_kn.dim() != 2 or b_kn.shape[0] != K:
+        raise ValueError(f"b_kn must be [K={K}, N]")
+    N = b_kn.shape[1]
+    _check_codes(a, b_kn.t(), K)
+    kb = _cdiv(K, 128)
+    if b_block not in BLOCKS:
+        raise ValueError(f"b_block must be one of {sorted(BLOCKS)}")
+    _check_scales(ra, (M, kb), "ra")
+    _check_scales(rb, (N if b_block == "1x128" else _cdiv(N, 128), kb), "rb")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check_out(out, (M, N))
+    nws = lib.fp8bw_gemm_blockwise_ws_bytes(M, N, K)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=a.device)
+    check(lib.fp8_scaled_gemm_blockwise_kn(
+        a.data_ptr(), a.stride(0), ra.data_ptr(), ra.stride(0), ra.stride(1), b_kn.data_ptr(),
+        b_kn.stride(0), rb.data_ptr(), rb.stride(0), rb.stride(1), BLOCKS[b_block], M, N, K,
+        out.data_ptr(), out.stride(0), OUT_DTYPES[out.dtype], ws.data_ptr(), nws, _stream(a)))
+    return out
+
+
 def fp8bw_gemm_num_configs():
     return load_library().fp8bw_gemm_num_configs()
 

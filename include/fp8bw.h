@@ -200,6 +200,34 @@ int fp8_scaled_gemm_blockwise(const void* a, int64_t lda, const float* ra, int64
                               void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * fp8_scaled_gemm_blockwise_kn -- the same GEMM with B given in [K, N]
+ * layout: out[M, N] = sum_kb ra[m, kb] * rb[beta(n), kb]
+ *                     * sum_{k in block kb} a[m, k] * b_kn[k, n].
+ * The second operand arrives as the transposed (column-major) view of an
+ * [N, K] matrix, the way torch._scaled_mm takes the weight ([AITER] Steps to
+ * Reproduce: the weight passed as its .t() view); e.g. dX = dY . W from W's
+ * own codes, whose 128x128 blocks and scales serve W^T unchanged (block amax
+ * does not depend on orientation), with no transposed copy of the codes.
+ *   b_kn device E4M3 [K, N], row stride ldb >= N (N contiguous).
+ *   rb   indexed by (output column n, K block) exactly as in
+ *        fp8_scaled_gemm_blockwise (for W's scales sw[nb_w][kb_w]: the view
+ *        with strides swapped).
+ * The kernel reads B's [K block, 256 columns] tiles into LDS row by row and
+ * forms the matrix-core operands with transposing LDS reads; outputs are
+ * bit-identical to fp8_scaled_gemm_blockwise on b = b_kn^T.
+ * Needs M >= 256, N >= 256, N % 16 == 0 (and N % 64 == 0 for 128x128 B
+ * scales), 256 * ldb + K < 2^31 and K % 128 == 0; other problems give
+ * FP8BW_ERR_UNSUPPORTED (use fp8_scaled_gemm_blockwise on a [N, K] copy).
+ * Workspace: fp8bw_gemm_blockwise_ws_bytes(M, N, K).  Other arguments and
+ * errors as fp8_scaled_gemm_blockwise.
+ */
+int fp8_scaled_gemm_blockwise_kn(const void* a, int64_t lda, const float* ra, int64_t ra_s_row,
+                                 int64_t ra_s_kb, const void* b_kn, int64_t ldb, const float* rb,
+                                 int64_t rb_s_row, int64_t rb_s_kb, int b_block, int64_t M,
+                                 int64_t N, int64_t K, void* out, int64_t ldo, int out_dtype,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Same as fp8_scaled_gemm_blockwise with an explicit tile configuration
  * (0 .. fp8bw_gemm_num_configs()-1, or -1 for the built-in choice) and
  * split-K count (>= 1, or 0 for the built-in choice).  Every configuration

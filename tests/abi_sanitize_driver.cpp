@@ -253,8 +253,28 @@ void gemm_validation() {
           }
           CHECK(known_status(fp8_scaled_gemm_tensorwise(buf_a, ld, s, buf_b, ld, s, M, N, K,
                                                         buf_out, ld, FP8BW_OUT_BF16, nullptr)));
+          for (int b_block : {FP8BW_BLOCK_128x128, FP8BW_BLOCK_1x128})
+            CHECK(known_status(fp8_scaled_gemm_blockwise_kn(
+                buf_a, ld, s, 1, ld, buf_b, ld, s, 1, ld, b_block, M, N, K, buf_out, ld,
+                FP8BW_OUT_BF16, buf_ws, sizeof(buf_ws), nullptr)));
         }
       }
+}
+
+// B in [K, N] layout: ldb >= N, and the large tiles' limits.
+void gemm_kn_validation() {
+  const float* s = buf_s;
+  auto kn = [&](int64_t M, int64_t N, int64_t K, int64_t ldb) {
+    return fp8_scaled_gemm_blockwise_kn(buf_a, 256, s, 1, 512, buf_b, ldb, s, 1, 4,
+                                        FP8BW_BLOCK_128x128, M, N, K, buf_out, 512,
+                                        FP8BW_OUT_BF16, nullptr, 0, nullptr);
+  };
+  EXPECT_STATUS(kn(512, 512, 256, 256), FP8BW_ERR_LAYOUT);          // ldb < N
+  EXPECT_STATUS(kn(512, 512, 256, kI64Max - 15), FP8BW_ERR_LAYOUT);  // past 2^48
+  EXPECT_STATUS(kn(128, 512, 256, 512), FP8BW_ERR_UNSUPPORTED);      // M < 256
+  EXPECT_STATUS(kn(512, 336, 256, 512), FP8BW_ERR_UNSUPPORTED);      // N % 64, 128x128 scales
+  EXPECT_STATUS(kn(512, 512, 256, (int64_t)1 << 23), FP8BW_ERR_UNSUPPORTED);  // 256 ldb >= 2^31
+  EXPECT_STATUS(kn(512, 512, 256, 512), FP8BW_ERR_HIP);              // valid; no GPU here
 }
 
 void grouped_validation() {
@@ -395,6 +415,7 @@ int main() {
   quant_validation();
   tensorwise_validation();
   gemm_validation();
+  gemm_kn_validation();
   grouped_validation();
   queries();
   linear_validation();

@@ -136,6 +136,24 @@ def test_gemm_validation(lib):
     assert _gemm(lib, "fp8_scaled_gemm_blockwise_cfg", splits=2, ws=None) == WS
 
 
+def test_gemm_kn_validation(lib):
+    """fp8_scaled_gemm_blockwise_kn: B is [K, N] (ldb >= N); it runs on the
+    256x256 tiles only and refuses smaller or unaligned problems before any
+    launch."""
+    kn = dict(fn="fp8_scaled_gemm_blockwise_kn", M=512, N=512, K=256, lda=256, ldb=512,
+              ldo=512, ra_s_kb=512, rb_s_kb=4)
+    assert _gemm(lib, **{**kn, "ldb": 256}) == LAYOUT      # ldb < N
+    assert _gemm(lib, **{**kn, "ldb": 520}) == LAYOUT      # not a multiple of 16
+    assert _gemm(lib, **{**kn, "b": None}) == NULL
+    assert _gemm(lib, **{**kn, "K": 200}) == SHAPE         # K % 128
+    assert _gemm(lib, **{**kn, "M": 128}) == UNSUP         # M < 256
+    assert _gemm(lib, **{**kn, "N": 200, "ldo": 200, "ldb": 208, "rb_s_kb": 2}) == UNSUP  # N < 256
+    assert _gemm(lib, **{**kn, "N": 264, "ldo": 264, "ldb": 272, "rb_s_kb": 3}) == UNSUP  # N % 16
+    assert _gemm(lib, **{**kn, "N": 336, "ldo": 336, "ldb": 336, "rb_s_kb": 3}) == UNSUP  # N % 64, 128x128
+    assert "[K, N]" in lib.fp8bw_last_error().decode()
+    assert _gemm(lib, **{**kn, "M": 0, "a": None, "b": None, "out": None}) == OK
+
+
 def test_bias_entry_points_validate(lib):
     """The _bias entry points share the GEMMs' validation and add a 2-byte
     alignment check on the bias pointer."""
