@@ -628,6 +628,59 @@ __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& p, const v4f
   }
 }
 
+// Epilogue of an interior 256x256 tile with fp32 values (an fp32 output with
+// its bias, or a K piece's partial), through LDS like the bf16 epilogue but
+// in two passes, the 256 KB tile being twice the 128 KB of stage arrays:
+// pass h takes the sub-tile rows 4h .. 4h + 3 of every wave, i.e. tile rows
+// 64 h .. 64 h + 63 and 128 + 64 h .. 128 + 64 h + 63, as 128 LDS rows of
+// 1 KB (LDS row r = 64 wm + 16 i' + frow in array r / 32; 16-byte chunk c at
+// c ^ (r & 15)).  Then wave w reads LDS rows 16 w .. 16 w + 15, one 1 KB row
+// per instruction, and stores each as eight whole lines (16-byte
+// nontemporal stores: the reduce that reads the partials runs on other
+// XCDs' L2s anyway).  base addresses the tile's element (0, 0), ld its row
+// stride in floats.
+template <int TM, int TN, int MODE, bool BIAS>
+__device__ __forceinline__ void store_tile_f32_lds(const GemmArgs& p, const v4f (&acc)[TM][TN],
+                                                   float tscale, uint8_t* s0, uint8_t* s1,
+                                                   uint8_t* s2, uint8_t* s3, float* base,
+                                                   int64_t ld, int n0, int wave, int lane) {
+  static_assert(TM == 8 && TN == 4, "256x256 tile of 8 waves of 128x64");
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  auto arr = [&](int q) -> uint8_t* { return q == 0 ? s0 : q == 1 ? s1 : q == 2 ? s2 : s3; };
+  const int wmi = wave / 4, wni = wave % 4;
+  const int frow = lane & 15, fhalf = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();   // the stages (pass 0) or the previous pass are read
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 4 * h + ii;
+      const int lr = 64 * wmi + 16 * ii + frow;
+      uint8_t* const rowp = arr(lr >> 5) + (lr & 31) * 1024;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = 64 * wni + 16 * j + 4 * fhalf;
+        float val[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          val[v] = acc[i][j][v];
+          if constexpr (MODE == kTensorwise) val[v] *= tscale;
+          if constexpr (BIAS) val[v] += bias_at(p.bias, n0 + col + v);
+        }
+        *(float4*)(rowp + 16 * ((col >> 2) ^ frow)) = make_float4(val[0], val[1], val[2], val[3]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int lr = 16 * wave + k;
+      const int trow = 128 * (lr >> 6) + 64 * h + (lr & 63);
+      const u32x4 d = *(const u32x4*)(arr(lr >> 5) + (lr & 31) * 1024 + 16 * (lane ^ (lr & 15)));
+      __builtin_nontemporal_store(d, (u32x4*)(base + (int64_t)trow * ld + 4 * lane));
+    }
+  }
+}
+
 // Number of tiles of a grouped GEMM's group table (each group's row tiles
 // times the column tiles), with the same clamping as locate_group_tile.
 template <int BM>
@@ -1028,17 +1081,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     }
   }
   const bool interior = ml == m0 && nl == n0 && m0 + BM <= p.M && n0 + BN <= p.N;
-  // bf16 output of an interior 256x256 tile: staged through LDS (free once
-  // the K loop is done) so that every global store writes whole 128-byte
-  // lines, 16 bytes a lane, instead of the 8-byte quads of four columns the
-  // MFMA layout leaves in each lane (each row of a wave's output then
-  // arriving in 32-byte pieces).  The stores are nontemporal: the output is
-  // not read again by this launch, and keeping it out of the L2 leaves the
-  // L2 to the operands (fwd/dgrad calls 2.6-2.8% faster, same bits).
-  if constexpr (BM == 256 && BN == 256 && WGM == 2 && WGN == 4 && OUT == kOutBf16 && !SPLIT) {
-    if (interior && (p.ldo & 7) == 0 && ((size_t)p.out & 15) == 0) {
-      store_tile_bf16_lds<TM, TN, MODE>(p, acc, tscale, sA0, sA1, sB0, sB1, m0, n0, wave, lane);
-      return;
+  // An interior 256x256 tile is staged through LDS (free once the K loop is
+  // done) so that every global store writes whole 128-byte lines, 16 bytes
+  // a lane, instead of the quads of four columns the MFMA layout leaves in
+  // each lane (a row of a wave's output then arriving in 32-byte (bf16) or
+  // 64-byte (fp32) pieces).  The stores are nontemporal: nothing in this
+  // launch reads the output again, and keeping it out of the L2 leaves the
+  // L2 to the operands.  Same bits; on the linear step's shapes the bf16
+  // tiles made the fwd and dgrad calls 2.6-2.8% faster, the fp32 partials
+  // of the leftover tiles another 0.7-1.6%.
+  if constexpr (BM == 256 && BN == 256 && WGM == 2 && WGN == 4) {
+    if constexpr (SPLIT) {
+      if (interior && (pld & 3) == 0 && ((size_t)pbase & 15) == 0) {
+        store_tile_f32_lds<TM, TN, MODE, false>(p, acc, tscale, sA0, sA1, sB0, sB1,
+                                                pbase + (int64_t)(m0 - pm0) * pld + (n0 - pn0),
+                                                pld, n0, wave, lane);
+        return;
+      }
+    } else if constexpr (OUT == kOutBf16) {
+      if (interior && (p.ldo & 7) == 0 && ((size_t)p.out & 15) == 0) {
+        store_tile_bf16_lds<TM, TN, MODE>(p, acc, tscale, sA0, sA1, sB0, sB1, m0, n0, wave, lane);
+        return;
+      }
+    } else {
+      if (interior && (p.ldo & 3) == 0 && ((size_t)p.out & 15) == 0) {
+        store_tile_f32_lds<TM, TN, MODE, true>(p, acc, tscale, sA0, sA1, sB0, sB1,
+                                               (float*)p.out + (int64_t)m0 * p.ldo + n0, p.ldo,
+                                               n0, wave, lane);
+        return;
+      }
     }
   }
   if (interior)

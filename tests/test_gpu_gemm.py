@@ -132,6 +132,41 @@ def test_every_config_and_split(gpu, mn, pad):
                                    splits=splits, ldo_pad=pad)
 
 
+@pytest.mark.parametrize("pad", [16, 4, 2])
+def test_large_tile_staged_epilogue_canary(gpu, pad):
+    """The 256x256 kernel stages interior tiles through LDS and stores whole
+    rows of the tile (bf16 when the output row stride is a multiple of 8
+    elements, fp32 outputs and K-split partials when it is a multiple of 4;
+    otherwise the direct quad stores).  M = 520, N = 576 gives four interior
+    tiles and five edge tiles; the output is a view 8 columns into a
+    NaN-filled buffer of row stride N + 8 + pad, and every column on either
+    side of it must keep its canary.  pad 16: all staged; 4: fp32 staged,
+    bf16 direct; 2: all direct."""
+    rng = np.random.default_rng(41 + pad)
+    M, N, kb = 520, 576, 3
+    aq = _random_codes(rng, (M, 128 * kb))
+    bq = _random_codes(rng, (N, 128 * kb))
+    ar = rng.uniform(0.01, 0.02, (M, kb)).astype(np.float32)
+    for b_block in ("128x128", "1x128"):
+        nbr = N if b_block == "1x128" else -(-N // 128)
+        br = rng.uniform(0.01, 0.02, (nbr, kb)).astype(np.float32)
+        ref, S = gemm.blockwise_gemm(aq, ar, bq, br, b_block, with_bound=True)
+        for od_name, od in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+            for splits in (1, 2):
+                what = f"staged epilogue {b_block} {od_name} split{splits} pad{pad}"
+                say("gemm", what)
+                buf = torch.full((M, N + 8 + pad), float("nan"), dtype=od, device=gpu)
+                out = buf[:, 8:8 + N]
+                fp8.fp8_scaled_gemm_blockwise(_up_codes(aq, gpu), _up_scales_colmajor(ar, gpu),
+                                              _up_codes(bq, gpu), _up_scales_colmajor(br, gpu),
+                                              b_block=b_block, out_dtype=od, config=3,
+                                              splits=splits, out=out)
+                torch.cuda.synchronize()
+                assert torch.isnan(buf[:, :8].float()).all(), f"{what}: wrote before column 0"
+                assert torch.isnan(buf[:, 8 + N:].float()).all(), f"{what}: wrote past N"
+                check_gemm_output(host_f32(out), ref, S, kb, od_name, what)
+
+
 def _scale_view(r, layout, dev):
     """Logical fp32 [ni, nj] on the device in a given memory layout."""
     r = np.asarray(r, np.float32)
