@@ -600,7 +600,14 @@ def gemm_plans(shape=(M, N, K)):
                                    ("gemm dgrad", (m, k, n, "128x128")),
                                    ("gemm wgrad", (n, k, m, "1x128"))):
         pl = fp8.gemm_plan(gm, gn, gk, mode)
-        parts = [f"main launch {pl['tiles_full'] if pl['tail_splits'] > 1 else pl['tiles']} tiles"]
+        nmain = pl['tiles_full'] if pl['tail_splits'] > 1 else pl['tiles']
+        parts = [f"main launch {nmain} tiles"]
+        # The library runs two or more full rounds of interior 256x256 tiles
+        # (bf16 out, contiguous rows) as a persistent launch.
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        if (pl["config"] == 3 and pl["splits"] == 1 and gm % 256 == 0 and gn % 256 == 0
+                and nmain >= 2 * cus and nmain % cus == 0):
+            parts[0] += f" ({cus} persistent workgroups x {nmain // cus})"
         if pl["splits"] > 1:
             parts[0] += f" x {pl['splits']} K splits"
             parts.append("ordered reduce")

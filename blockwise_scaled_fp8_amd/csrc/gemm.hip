@@ -73,6 +73,10 @@ struct GemmArgs {
   // B given in [K, N] layout (b[k * ldb + n], N contiguous) instead of
   // [N, K]; large 256x256 tiles only.
   int b_kn;
+  // Persistent launch (gemm_v2_kernel with PERSIST): each workgroup runs
+  // `rounds` tiles in turn, those a grid of rounds x gridDim.x workgroups
+  // would have run; other launches leave it at 1.
+  int rounds;
 };
 
 // A grouped GEMM on the large tiles runs as two launches: the large-tile
@@ -412,6 +416,18 @@ __device__ __forceinline__ void stage_sync() {
   __builtin_amdgcn_s_barrier();
 }
 
+// End of a K block for a wave that issues no direct loads: its LDS reads have
+// returned, then the barrier.  It does not wait on vmcnt, so output stores it
+// left in flight (persistent launch) keep draining under the K loop.
+__device__ __forceinline__ void stage_sync_noload() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+  __builtin_amdgcn_s_barrier();
+}
+
+// Which copy of the K loop a wave runs: 0 the common one (every wave, loads
+// issued by waves < LW), 1 a loader wave's, 2 a non-loader wave's.
+template <int R> struct kloop_role { static constexpr int value = R; };
+
 // Tile order: XCD-aware (the dispatcher deals workgroups round-robin to the
 // 8 XCDs in linear workgroup order; xcd_remap gives each XCD a contiguous
 // range of ids) then
@@ -583,7 +599,14 @@ __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM
 // wave must have waited for its own direct loads (vmcnt 0) before the call;
 // the first barrier orders every wave's last fragment reads before the
 // first write.
-template <int TM, int TN, int MODE>
+// With STORERS0 > 0 (persistent launch) only waves STORERS0 .. 7 (the ones
+// that issue no direct loads) store, two rows per instruction over the 256
+// rows, and nothing waits for the stores: the call ends with their LDS reads
+// returned and a barrier, so the next tile's loads may fill the stages while
+// the stores drain.  (A wave's s_endpgm waits for all its outstanding stores;
+// with one tile per workgroup every round of tiles ended with the whole
+// chip's output, 32 MB, draining while no CU computed.)
+template <int TM, int TN, int MODE, int STORERS0 = 0>
 __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& p, const v4f (&acc)[TM][TN],
                                                     float tscale, uint8_t* s0, uint8_t* s1,
                                                     uint8_t* s2, uint8_t* s3, int m0, int n0,
@@ -594,7 +617,10 @@ __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& p, const v4f
   auto arr = [&](int q) -> uint8_t* { return q == 0 ? s0 : q == 1 ? s1 : q == 2 ? s2 : s3; };
   const int wmi = wave / 4, wni = wave % 4;
   const int frow = lane & 15, fhalf = lane >> 4;
-  __syncthreads();   // every wave is done reading the stages
+  if constexpr (STORERS0 > 0)
+    stage_sync_noload();   // every wave is done reading the stages
+  else
+    __syncthreads();
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     uint8_t* const qb = arr(2 * wmi + i / 4);
@@ -616,15 +642,30 @@ __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& p, const v4f
       *(u32x2*)(qb + rq * 512 + 16 * (chunk ^ frow) + 8 * (fhalf & 1)) = w;
     }
   }
-  __syncthreads();
-  const int q = wave >> 1, rbase = 32 * (wave & 1), c = lane & 31;
-  const uint8_t* const qr = arr(q);
-  uint16_t* const ob = (uint16_t*)p.out + (int64_t)(m0 + 64 * q) * p.ldo + n0;
+  const int c = lane & 31;
+  if constexpr (STORERS0 > 0) {
+    stage_sync_noload();
+    if (wave >= STORERS0) {
+      uint16_t* const ob = (uint16_t*)p.out + (int64_t)m0 * p.ldo + n0;
+      for (int pr = wave - STORERS0; pr < 128; pr += 8 - STORERS0) {
+        const int row = 2 * pr + (lane >> 5);   // tile row, in array row / 64
+        const int rr = row & 63;
+        const u32x4 d = *(const u32x4*)(arr(row >> 6) + rr * 512 + 16 * (c ^ (rr & 15)));
+        __builtin_nontemporal_store(d, (u32x4*)(ob + (int64_t)row * p.ldo + 8 * c));
+      }
+    }
+    stage_sync_noload();   // the stages are free again
+  } else {
+    __syncthreads();
+    const int q = wave >> 1, rbase = 32 * (wave & 1);
+    const uint8_t* const qr = arr(q);
+    uint16_t* const ob = (uint16_t*)p.out + (int64_t)(m0 + 64 * q) * p.ldo + n0;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int row = rbase + 2 * k + (lane >> 5);
-    const u32x4 d = *(const u32x4*)(qr + row * 512 + 16 * (c ^ (row & 15)));
-    __builtin_nontemporal_store(d, (u32x4*)(ob + (int64_t)row * p.ldo + 8 * c));
+    for (int k = 0; k < 16; ++k) {
+      const int row = rbase + 2 * k + (lane >> 5);
+      const u32x4 d = *(const u32x4*)(qr + row * 512 + 16 * (c ^ (row & 15)));
+      __builtin_nontemporal_store(d, (u32x4*)(ob + (int64_t)row * p.ldo + 8 * c));
+    }
   }
 }
 
@@ -731,7 +772,7 @@ __device__ __forceinline__ bool locate_group_tile(GemmArgs& p, int t, int* tm, i
 }
 
 template <int BM, int BN, int WGM, int WGN, int STAGES, int MODE, int OUT, bool SPLIT,
-          bool BKN = false>
+          bool BKN = false, bool PERSIST = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs p_in) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -777,6 +818,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
+  // Persistent launch (full rounds of interior 256x256 tiles, bf16 out, no
+  // split): one workgroup per CU runs p_in.rounds tiles, the ones that
+  // workgroups blockIdx.x + r * gridDim.x of a one-tile-per-workgroup grid
+  // would run, so the tile order is unchanged.
+  static_assert(!PERSIST || (BM == 256 && BN == 256 && NW == 8 && OUT == kOutBf16 && !SPLIT &&
+                             !BKN),
+                "persistent launch: 256x256 bf16 tiles only");
+  const int rounds = PERSIST ? p_in.rounds : 1;
+  auto run_tile = [&](int rnd) {
   int tm, tn;
   GemmArgs p = p_in;
   // Workgroup -> (K split, tile): the whole grid, split-major, dealt out
@@ -788,7 +838,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   // tiles are dealt out over the tiles that exist, so that the workgroups
   // past them are the last of every XCD rather than a run on the last XCDs
   // (which left the other XCDs a partly filled extra round).
-  const int nwg = gridDim.x * gridDim.y;
+  const int gx = gridDim.x * rounds;
+  const int nwg = gx * gridDim.y;
   int wg;
   if (p.groups > 0) {
     if (p.group_part == 1 && !grouped_split_pays(p)) p.group_part = 0;
@@ -799,10 +850,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     if (q >= full + (x < rem ? 1 : 0)) return;
     wg = x * full + min(x, rem) + q;
   } else {
-    wg = xcd_remap(blockIdx.y * gridDim.x + blockIdx.x, nwg);
+    wg = xcd_remap(blockIdx.y * gx + blockIdx.x + rnd * gridDim.x, nwg);
   }
-  const int split = wg / gridDim.x;
-  const int tile_local = wg - split * gridDim.x;
+  const int split = wg / gx;
+  const int tile_local = wg - split * gx;
   // Output tile [m0, m0 + BM) x [n0, n0 + BN).  The operand window the tile
   // loads, [ml, ml + BM) x [nl, nl + BN), is the same except at a ragged
   // edge, where it moves back to end exactly at the last row of A (of B):
@@ -884,12 +935,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const int64_t rb_bytes = MODE == kBlockB128 ? ((int64_t)((p.N - 1) / 128) * p.rb_s_row + 1) * 4
                                               : ((int64_t)(BN - 1) * p.rb_s_row + 1) * 4;
 
-#define FP8BW_ISSUE(kb, st)                                                                   \
-  if (wave < LW)                                                                              \
-  issue_stage<AI, BI, RAI, RBI, RAB, RBB, LW, MODE, BKN>(                                     \
-      p, (kb), sA[st], sB[st], sRa[st], sRb[st], ars, brs, a_voff, BKN ? bkn_voff : b_voff,    \
-      b_voff_hi, p.b + nl, BN, ra_voff, rb_voff, ra_base, ra_bytes, rb_base, rb_bytes, wave)
-
   v4f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -904,13 +949,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   // always has exactly LPS loads per stage in flight.
   const int kb_last = kb_end - 1;
 
+  // The K loop.  A persistent launch runs it in two copies, one per wave
+  // role, so that neither has a branch on the role inside the loop (one
+  // there made the compiler spill): the loader waves issue the direct loads
+  // and wait for them, the other waves never wait on vmcnt, which lets the
+  // output stores they issued for the previous tile drain meanwhile.
+#define FP8BW_ISSUE_ROLE(kb, st)                                                              \
+  if (kRole == 1 || (kRole == 0 && wave < LW))                                                \
+  issue_stage<AI, BI, RAI, RBI, RAB, RBB, LW, MODE, BKN>(                                     \
+      p, (kb), sA[st], sB[st], sRa[st], sRb[st], ars, brs, a_voff, BKN ? bkn_voff : b_voff,    \
+      b_voff_hi, p.b + nl, BN, ra_voff, rb_voff, ra_base, ra_bytes, rb_base, rb_bytes, wave)
+  auto kloop = [&](auto role) {
+  constexpr int kRole = decltype(role)::value;
   if (nkb > 0) {
-    FP8BW_ISSUE(kb_begin, 0);
+    FP8BW_ISSUE_ROLE(kb_begin, 0);
     if constexpr (STAGES == 3) {
-      FP8BW_ISSUE(min(kb_begin + 1, kb_last), 1);
-      wait_vmcnt<LPS>();
+      FP8BW_ISSUE_ROLE(min(kb_begin + 1, kb_last), 1);
+      if constexpr (kRole != 2) wait_vmcnt<LPS>();
     } else {
-      wait_vmcnt<0>();
+      if constexpr (kRole != 2) wait_vmcnt<0>();
     }
     __builtin_amdgcn_s_barrier();
   }
@@ -919,7 +976,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   for (int st = 0; st < STAGES; ++st) {
     const int it = it0 + st;
     if (it >= nkb) break;
-    FP8BW_ISSUE(min(kb_begin + it + STAGES - 1, kb_last), (st + STAGES - 1) % STAGES);
+    FP8BW_ISSUE_ROLE(min(kb_begin + it + STAGES - 1, kb_last), (st + STAGES - 1) % STAGES);
 
     // LDS byte offsets of this lane's fragment chunks and scales.  Sub-tile
     // i of a wave is 16 rows (2 KB) further down and keeps the same swizzle,
@@ -1054,13 +1111,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
         }
       }
     }
-    if constexpr (STAGES == 3)
+    if constexpr (kRole == 2)
+      stage_sync_noload();
+    else if constexpr (STAGES == 3)
       stage_sync<LPS>();
     else
       stage_sync<0>();
   }
   }
-  wait_vmcnt<0>();
+  if constexpr (kRole != 2) wait_vmcnt<0>();
+  };
+  if constexpr (PERSIST) {
+    if (wave < LW) kloop(kloop_role<1>{});
+    else kloop(kloop_role<2>{});
+  } else {
+    kloop(kloop_role<0>{});
+  }
+#undef FP8BW_ISSUE_ROLE
 
   float tscale = 1.f;
   if constexpr (MODE == kTensorwise) tscale = p.ra[0] * p.rb[0];
@@ -1081,6 +1148,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
     }
   }
   const bool interior = ml == m0 && nl == n0 && m0 + BM <= p.M && n0 + BN <= p.N;
+  if constexpr (PERSIST) {
+    // Every tile of a persistent launch is interior (the host checks M, N,
+    // the output stride and alignment).  (A second epilogue for the last
+    // tile, stored by all eight waves, made the kernel spill.)
+    store_tile_bf16_lds<TM, TN, MODE, LW>(p, acc, tscale, sA0, sA1, sB0, sB1, m0, n0, wave, lane);
+    return;
+  }
   // An interior 256x256 tile is staged through LDS (free once the K loop is
   // done) so that every global store writes whole 128-byte lines, 16 bytes
   // a lane, instead of the quads of four columns the MFMA layout leaves in
@@ -1118,8 +1192,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   else
     store_acc<true, TM, TN, MODE, OUT, SPLIT>(p, acc, tscale, ml + wm0, nl + wn0, m0, n0, frow,
                                               fhalf, pbase, pld, pm0, pn0);
+  };
+  if constexpr (PERSIST) {
+#pragma nounroll
+    for (int rnd = 0; rnd < rounds; ++rnd) run_tile(rnd);
+  } else {
+    run_tile(0);
+  }
 }
-#undef FP8BW_ISSUE
 
 // Sum the split partials [split][M][N] in split order and convert.  With
 // N % 4 == 0 a thread takes four consecutive columns (16-byte partial loads,
@@ -1346,6 +1426,16 @@ static int heuristic_config(const GemmProblem& p, bool allow_split, int cus) {
   return 1;
 }
 
+// The main launch may run persistent (gemm_v2_kernel with PERSIST): 256x256
+// tiles, [N, K] B, bf16 output, no K split, at least two whole rounds of
+// tiles (one per CU), every tile interior (M and N multiples of 256) and
+// output rows the staged epilogue can store whole (16-byte aligned rows).
+static bool persistent_ok(const GemmProblem& p, int cfg, int splits, int nmain, int cus) {
+  return cfg == 3 && !p.b_kn && splits == 1 && p.out_kind == kOutBf16 && cus > 0 &&
+         nmain >= 2 * cus && nmain % cus == 0 && p.K >= 128 && p.M % 256 == 0 &&
+         p.N % 256 == 0 && p.ldo % 8 == 0 && ((size_t)p.out & 15) == 0;
+}
+
 GemmPlan gemm_plan(const GemmProblem& p, int config, int splits, bool allow_split) {
   GemmPlan pl;
   const int cus = num_cus();
@@ -1410,6 +1500,13 @@ static hipError_t launch_v2(const GemmArgs& a, int ntiles, int splits, int out_k
                             hipStream_t stream) {
   dim3 grid((unsigned)ntiles, (unsigned)splits);
   dim3 block(64 * WGM * WGN);
+  if constexpr (BM == 256 && BN == 256 && WGM == 2 && WGN == 4 && !BKN) {
+    if (a.rounds > 1) {   // persistent: ntiles workgroups of a.rounds tiles each
+      hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutBf16, false, false, true>),
+                         grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (splits > 1)
     hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, WGM, WGN, STAGES, MODE, kOutF32, true, BKN>), grid, block, 0, stream, a);
   else if (out_kind == kOutBf16)
@@ -1505,6 +1602,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
   a.part_tiled = 0;
   a.bias = (const uint16_t*)p.bias;
   a.b_kn = p.b_kn;
+  a.rounds = 1;
   a.groups = 0;
   a.group_part = 0;
   a.group_cus = 1;
@@ -1520,7 +1618,16 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
   } else {
     // Full rounds (or the whole problem) unsplit or whole-problem split-K.
     const int nmain = (int)(pl.tail_splits > 1 ? pl.tiles_full : pl.tiles);
-    e = nmain > 0 ? launch_v2_cfg(cfg, a, p.mode, nmain, splits, p.out_kind, stream) : hipSuccess;
+    const int cus = num_cus();
+    if (persistent_ok(p, cfg, splits, nmain, cus)) {
+      // Two or more full rounds of interior tiles: one workgroup per CU runs
+      // its tiles of every round (bit-identical output, 1-2% faster).
+      GemmArgs m = a;
+      m.rounds = nmain / cus;
+      e = launch_v2_cfg(cfg, m, p.mode, cus, 1, p.out_kind, stream);
+    } else {
+      e = nmain > 0 ? launch_v2_cfg(cfg, a, p.mode, nmain, splits, p.out_kind, stream) : hipSuccess;
+    }
     if (e == hipSuccess && pl.tail_splits > 1) {
       // Leftover tiles split over K into tile-local partials, then reduced.
       GemmArgs t = a;

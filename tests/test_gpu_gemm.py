@@ -167,6 +167,55 @@ def test_large_tile_staged_epilogue_canary(gpu, pad):
                 check_gemm_output(host_f32(out), ref, S, kb, od_name, what)
 
 
+@pytest.mark.parametrize("mode", ["128x128", "1x128", "tensorwise"])
+def test_persistent_main_launch(gpu, mode):
+    """Two full rounds of interior 256x256 tiles (one tile per CU each) run as
+    a persistent launch: one workgroup per CU takes its tile of every round
+    in turn, and the waves that issue no operand loads store each tile's
+    output while the next tile's K loop runs.  The same GEMM into an output
+    whose row stride is not a multiple of 8 elements runs one tile per
+    workgroup with the direct quad stores: the two must agree bit for bit,
+    and with the oracle on sampled rows (first, middle and last 64)."""
+    cus = torch.cuda.get_device_properties(gpu).multi_processor_count
+    if cus % 8:
+        pytest.skip(f"{cus} CUs: the shape below assumes a multiple of 8")
+    M, N, K = 4096, 32 * cus, 384     # 16 x (cus / 8) tiles = two rounds
+    kb = K // 128
+    pl = fp8.gemm_plan(M, N, K, "1x128" if mode == "1x128" else "128x128")
+    assert pl["config"] == 3 and pl["tail_splits"] == 1 and pl["tiles"] == 2 * cus, pl
+    rng = np.random.default_rng(61 + len(mode))
+    aq = _random_codes(rng, (M, K))
+    bq = _random_codes(rng, (N, K))
+    rows = np.r_[0:64, M // 2 - 32:M // 2 + 32, M - 64:M]
+    a_d, b_d = _up_codes(aq, gpu), _up_codes(bq, gpu)
+    if mode == "tensorwise":
+        ra, rb = np.float32(0.0123), np.float32(0.0456)
+        ref = gemm.tensorwise_gemm(aq[rows], ra, bq, rb)
+        S = gemm.tensorwise_bound(aq[rows], ra, bq, rb)
+        ra_d, rb_d = torch.tensor([ra], device=gpu), torch.tensor([rb], device=gpu)
+        call = lambda out: fp8.fp8_scaled_gemm_tensorwise(a_d, ra_d, b_d, rb_d, out=out)
+    else:
+        ar = rng.uniform(0.01, 0.02, (M, kb)).astype(np.float32)
+        nbr = N if mode == "1x128" else N // 128
+        br = rng.uniform(0.01, 0.02, (nbr, kb)).astype(np.float32)
+        ref, S = gemm.blockwise_gemm(aq[rows], ar[rows], bq, br, mode, with_bound=True)
+        ra_d, rb_d = _up_scales_colmajor(ar, gpu), _up_scales_colmajor(br, gpu)
+        call = lambda out: fp8.fp8_scaled_gemm_blockwise(a_d, ra_d, b_d, rb_d, b_block=mode,
+                                                         out=out)
+    outs = []
+    for pad in (0, 4):    # row stride N: persistent; N + 4: one tile per workgroup
+        say("gemm persistent", mode, M, N, K, "ldo pad", pad)
+        buf = torch.full((M, N + pad), float("nan"), dtype=torch.bfloat16, device=gpu)
+        call(buf[:, :N])
+        torch.cuda.synchronize()
+        if pad:
+            assert torch.isnan(buf[:, N:].float()).all(), "wrote past N"
+        outs.append(buf[:, :N])
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), \
+        "persistent and one-tile-per-workgroup launches differ"
+    check_gemm_output(host_f32(outs[0])[rows], ref, S, kb, "bf16", f"persistent {mode}")
+
+
 def _scale_view(r, layout, dev):
     """Logical fp32 [ni, nj] on the device in a given memory layout."""
     r = np.asarray(r, np.float32)
