@@ -75,8 +75,13 @@ struct GemmArgs {
   int b_kn;
   // Persistent launch (gemm_v2_kernel with PERSIST): each workgroup runs
   // `rounds` tiles in turn, those a grid of rounds x gridDim.x workgroups
-  // would have run; other launches leave it at 1.
+  // would have run; other launches leave it at 1.  Then workgroups
+  // 0 .. tail_pieces - 1 each run one K piece of the leftover tiles
+  // [tail_base, tail_base + tail_tiles) (tail_kbps K blocks a piece, fp32
+  // tile-local partials [piece split][tile - tail_base][BM][BN], the same
+  // pieces and workgroup order as the separate split launch); 0: none.
   int rounds;
+  int tail_pieces, tail_kbps, tail_base, tail_tiles;
 };
 
 // A grouped GEMM on the large tiles runs as two launches: the large-tile
@@ -826,9 +831,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
                              !BKN),
                 "persistent launch: 256x256 bf16 tiles only");
   const int rounds = PERSIST ? p_in.rounds : 1;
-  auto run_tile = [&](int rnd) {
+  auto run_tile = [&](int rnd, bool piece) {
   int tm, tn;
   GemmArgs p = p_in;
+  if (piece) {   // persistent launch: a leftover tile's K piece
+    p.tile_base = p_in.tail_base;
+    p.kb_per_split = p_in.tail_kbps;
+  }
   // Workgroup -> (K split, tile): the whole grid, split-major, dealt out
   // XCD-contiguously, so the workgroups an XCD runs together mostly share
   // one K range and read the same A and B slices through its L2 (with the
@@ -852,8 +861,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   } else {
     wg = xcd_remap(blockIdx.y * gx + blockIdx.x + rnd * gridDim.x, nwg);
   }
-  const int split = wg / gx;
-  const int tile_local = wg - split * gx;
+  int split = wg / gx;
+  int tile_local = wg - split * gx;
+  if (piece) {
+    const int w2 = xcd_remap(blockIdx.x, p_in.tail_pieces);
+    split = w2 / p_in.tail_tiles;
+    tile_local = w2 - split * p_in.tail_tiles;
+  }
   // Output tile [m0, m0 + BM) x [n0, n0 + BN).  The operand window the tile
   // loads, [ml, ml + BM) x [nl, nl + BN), is the same except at a ragged
   // edge, where it moves back to end exactly at the last row of A (of B):
@@ -1150,8 +1164,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   const bool interior = ml == m0 && nl == n0 && m0 + BM <= p.M && n0 + BN <= p.N;
   if constexpr (PERSIST) {
     // Every tile of a persistent launch is interior (the host checks M, N,
-    // the output stride and alignment).  (A second epilogue for the last
-    // tile, stored by all eight waves, made the kernel spill.)
+    // the output stride and alignment).  (A second bf16 epilogue for the
+    // last tile, stored by all eight waves, made the kernel spill.)
+    if (piece) {
+      float* const pb = p.partial + ((int64_t)split * p_in.tail_tiles + tile_local) * (BM * BN);
+      store_tile_f32_lds<TM, TN, MODE, false>(p, acc, tscale, sA0, sA1, sB0, sB1, pb, BN, n0,
+                                              wave, lane);
+      return;
+    }
     store_tile_bf16_lds<TM, TN, MODE, LW>(p, acc, tscale, sA0, sA1, sB0, sB1, m0, n0, wave, lane);
     return;
   }
@@ -1195,9 +1215,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_v2_kernel(const GemmArgs 
   };
   if constexpr (PERSIST) {
 #pragma nounroll
-    for (int rnd = 0; rnd < rounds; ++rnd) run_tile(rnd);
+    for (int rnd = 0; rnd < rounds; ++rnd) run_tile(rnd, false);
+    if ((int)blockIdx.x < p_in.tail_pieces) run_tile(0, true);
   } else {
-    run_tile(0);
+    run_tile(0, false);
   }
 }
 
@@ -1603,6 +1624,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
   a.bias = (const uint16_t*)p.bias;
   a.b_kn = p.b_kn;
   a.rounds = 1;
+  a.tail_pieces = 0;
   a.groups = 0;
   a.group_part = 0;
   a.group_cus = 1;
@@ -1619,23 +1641,35 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& pl, void* ws, hipSt
     // Full rounds (or the whole problem) unsplit or whole-problem split-K.
     const int nmain = (int)(pl.tail_splits > 1 ? pl.tiles_full : pl.tiles);
     const int cus = num_cus();
-    if (persistent_ok(p, cfg, splits, nmain, cus)) {
+    // Leftover tiles split over K into tile-local partials, then reduced.
+    GemmArgs t = a;
+    const int ntail = (int)(pl.tiles - pl.tiles_full);
+    t.tile_base = (int)pl.tiles_full;
+    t.part_tiled = 1;
+    t.kb_per_split = (a.kblocks + pl.tail_splits - 1) / pl.tail_splits;
+    // (Every piece needs a workgroup of the persistent grid: ntail * tail
+    // splits <= cus, which the plan's choice of splits gives.)
+    const bool persist = persistent_ok(p, cfg, splits, nmain, cus) &&
+                         (pl.tail_splits <= 1 || (int64_t)ntail * pl.tail_splits <= cus);
+    if (persist) {
       // Two or more full rounds of interior tiles: one workgroup per CU runs
-      // its tiles of every round (bit-identical output, 1-2% faster).
+      // its tiles of every round, then the leftover tiles' K pieces (each
+      // piece's workgroup is free from its last tile on, with that tile's
+      // stores still draining): bit-identical output, 1-2% faster.
       GemmArgs m = a;
       m.rounds = nmain / cus;
+      if (pl.tail_splits > 1) {
+        m.tail_pieces = ntail * pl.tail_splits;
+        m.tail_kbps = t.kb_per_split;
+        m.tail_base = t.tile_base;
+        m.tail_tiles = ntail;
+      }
       e = launch_v2_cfg(cfg, m, p.mode, cus, 1, p.out_kind, stream);
     } else {
       e = nmain > 0 ? launch_v2_cfg(cfg, a, p.mode, nmain, splits, p.out_kind, stream) : hipSuccess;
     }
     if (e == hipSuccess && pl.tail_splits > 1) {
-      // Leftover tiles split over K into tile-local partials, then reduced.
-      GemmArgs t = a;
-      const int ntail = (int)(pl.tiles - pl.tiles_full);
-      t.tile_base = (int)pl.tiles_full;
-      t.part_tiled = 1;
-      t.kb_per_split = (a.kblocks + pl.tail_splits - 1) / pl.tail_splits;
-      e = launch_v2_cfg(cfg, t, p.mode, ntail, pl.tail_splits, p.out_kind, stream);
+      if (!persist) e = launch_v2_cfg(cfg, t, p.mode, ntail, pl.tail_splits, p.out_kind, stream);
       if (e == hipSuccess)
         e = cfg == 2 ? launch_tiled_reduce<256, 128>(t, pl.tail_splits, ntail, p.out_kind, stream)
                      : launch_tiled_reduce<256, 256>(t, pl.tail_splits, ntail, p.out_kind, stream);

@@ -167,23 +167,31 @@ def test_large_tile_staged_epilogue_canary(gpu, pad):
                 check_gemm_output(host_f32(out), ref, S, kb, od_name, what)
 
 
-@pytest.mark.parametrize("mode", ["128x128", "1x128", "tensorwise"])
-def test_persistent_main_launch(gpu, mode):
+@pytest.mark.parametrize("mode,leftover", [("128x128", False), ("1x128", False),
+                                           ("tensorwise", False), ("128x128", True),
+                                           ("1x128", True)])
+def test_persistent_main_launch(gpu, mode, leftover):
     """Two full rounds of interior 256x256 tiles (one tile per CU each) run as
     a persistent launch: one workgroup per CU takes its tile of every round
     in turn, and the waves that issue no operand loads store each tile's
-    output while the next tile's K loop runs.  The same GEMM into an output
-    whose row stride is not a multiple of 8 elements runs one tile per
-    workgroup with the direct quad stores: the two must agree bit for bit,
-    and with the oracle on sampled rows (first, middle and last 64)."""
+    output while the next tile's K loop runs; with leftover tiles (a 17th
+    row of tiles, cus / 8 of them), the workgroups then run those tiles' K
+    pieces before the reduce.  The same GEMM into an output whose row stride
+    is not a multiple of 8 elements runs one tile per workgroup with the
+    direct quad stores and a separate launch for the pieces: the two must
+    agree bit for bit, and with the oracle on sampled rows (first, middle
+    and last 64; the last are the leftover tiles' rows)."""
     cus = torch.cuda.get_device_properties(gpu).multi_processor_count
     if cus % 8:
         pytest.skip(f"{cus} CUs: the shape below assumes a multiple of 8")
-    M, N, K = 4096, 32 * cus, 384     # 16 x (cus / 8) tiles = two rounds
+    # 16 (17) x (cus / 8) tiles = two rounds (+ cus / 8 leftover tiles, split
+    # in 4 K pieces of 4 K blocks)
+    M, N, K = (4352, 32 * cus, 2048) if leftover else (4096, 32 * cus, 384)
     kb = K // 128
     pl = fp8.gemm_plan(M, N, K, "1x128" if mode == "1x128" else "128x128")
-    assert pl["config"] == 3 and pl["tail_splits"] == 1 and pl["tiles"] == 2 * cus, pl
-    rng = np.random.default_rng(61 + len(mode))
+    assert pl["config"] == 3 and pl["tiles_full"] == 2 * cus, pl
+    assert pl["tail_splits"] == (4 if leftover else 1), pl
+    rng = np.random.default_rng(61 + len(mode) + leftover)
     aq = _random_codes(rng, (M, K))
     bq = _random_codes(rng, (N, K))
     rows = np.r_[0:64, M // 2 - 32:M // 2 + 32, M - 64:M]
@@ -204,9 +212,9 @@ def test_persistent_main_launch(gpu, mode):
                                                          out=out)
     outs = []
     for pad in (0, 4):    # row stride N: persistent; N + 4: one tile per workgroup
-        say("gemm persistent", mode, M, N, K, "ldo pad", pad)
+        say("gemm persistent", mode, M, N, K, "ldo pad", pad, "leftover", leftover)
         buf = torch.full((M, N + pad), float("nan"), dtype=torch.bfloat16, device=gpu)
-        call(buf[:, :N])
+        call(buf[:, :N])   # (the binding allocates the workspace the plan asks for)
         torch.cuda.synchronize()
         if pad:
             assert torch.isnan(buf[:, N:].float()).all(), "wrote past N"
