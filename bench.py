@@ -601,18 +601,26 @@ def gemm_plans(shape=(M, N, K)):
                                    ("gemm wgrad", (n, k, m, "1x128"))):
         pl = fp8.gemm_plan(gm, gn, gk, mode)
         nmain = pl['tiles_full'] if pl['tail_splits'] > 1 else pl['tiles']
+        ntail = pl['tiles'] - pl['tiles_full']
         parts = [f"main launch {nmain} tiles"]
         # The library runs two or more full rounds of interior 256x256 tiles
-        # (bf16 out, contiguous rows) as a persistent launch.
+        # (bf16 out, contiguous rows) as a persistent launch, the leftover
+        # tiles' K pieces included.
         cus = torch.cuda.get_device_properties(0).multi_processor_count
-        if (pl["config"] == 3 and pl["splits"] == 1 and gm % 256 == 0 and gn % 256 == 0
-                and nmain >= 2 * cus and nmain % cus == 0):
-            parts[0] += f" ({cus} persistent workgroups x {nmain // cus})"
+        persist = (pl["config"] == 3 and pl["splits"] == 1 and gm % 256 == 0 and gn % 256 == 0
+                   and nmain >= 2 * cus and nmain % cus == 0
+                   and (pl["tail_splits"] <= 1 or ntail * pl["tail_splits"] <= cus))
+        if persist:
+            parts[0] += f" ({cus} persistent workgroups x {nmain // cus}"
+            if pl["tail_splits"] > 1:
+                parts[0] += f", then {ntail} leftover tiles x {pl['tail_splits']} K pieces"
+            parts[0] += ")"
         if pl["splits"] > 1:
             parts[0] += f" x {pl['splits']} K splits"
             parts.append("ordered reduce")
         if pl["tail_splits"] > 1:
-            parts.append(f"{pl['tiles'] - pl['tiles_full']} leftover tiles x {pl['tail_splits']} K splits")
+            if not persist:
+                parts.append(f"{ntail} leftover tiles x {pl['tail_splits']} K splits")
             parts.append("ordered reduce")
         out[nm] = dict(pl, launches=" + ".join(parts))
     return out
