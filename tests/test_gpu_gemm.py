@@ -454,6 +454,7 @@ def test_tail_split_of_last_round(mode, od):
     ((256, 256, 16384), "128x128", "f32"),     # whole-problem split-K: bias in the reduce
     ((2048, 2048, 1024), "128x128", "bf16"),   # large-tile kernel
     ((4352, 4096, 2048), "128x128", "f32"),    # full rounds + tail split (tiled reduce)
+    ((4352, 8192, 2048), "1x128", "bf16"),     # 256 CUs: persistent launch + leftover pieces
 ])
 def test_blockwise_bias_epilogue(gpu, mnk, b_block, od):
     """out = acc + bias[n] before the cast, on every store path the built-in
