@@ -622,10 +622,9 @@ __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& p, const v4f
   auto arr = [&](int q) -> uint8_t* { return q == 0 ? s0 : q == 1 ? s1 : q == 2 ? s2 : s3; };
   const int wmi = wave / 4, wni = wave % 4;
   const int frow = lane & 15, fhalf = lane >> 4;
-  if constexpr (STORERS0 > 0)
-    stage_sync_noload();   // every wave is done reading the stages
-  else
-    __syncthreads();
+  // (On gfx950 a workgroup-scope fence waits for LDS accesses only, so the
+  // barriers below leave the storing waves' global stores in flight.)
+  __syncthreads();   // every wave is done reading the stages
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     uint8_t* const qb = arr(2 * wmi + i / 4);
@@ -648,8 +647,8 @@ __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& p, const v4f
     }
   }
   const int c = lane & 31;
+  __syncthreads();
   if constexpr (STORERS0 > 0) {
-    stage_sync_noload();
     if (wave >= STORERS0) {
       uint16_t* const ob = (uint16_t*)p.out + (int64_t)m0 * p.ldo + n0;
       for (int pr = wave - STORERS0; pr < 128; pr += 8 - STORERS0) {
@@ -659,9 +658,8 @@ __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& p, const v4f
         __builtin_nontemporal_store(d, (u32x4*)(ob + (int64_t)row * p.ldo + 8 * c));
       }
     }
-    stage_sync_noload();   // the stages are free again
+    __syncthreads();   // the stages are free again
   } else {
-    __syncthreads();
     const int q = wave >> 1, rbase = 32 * (wave & 1);
     const uint8_t* const qr = arr(q);
     uint16_t* const ob = (uint16_t*)p.out + (int64_t)(m0 + 64 * q) * p.ldo + n0;
