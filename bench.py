@@ -8,13 +8,13 @@ at its loaded level: after only 5 warm-up steps the timed steps measured
 about 1.5% slower.
 
 A step is one pass of the whole hot path over one batch of synthetic input
-already resident in HBM, each bf16 tensor quantized once into both code
-layouts (the sequence fp8_linear_fwd_save and fp8_linear_bwd enqueue, which
+already resident in HBM, X and dY each quantized once into both code layouts
+(the sequence fp8_linear_fwd_save and fp8_linear_bwd enqueue, which
 Float8BlockwiseLinear trains through):
-  fwd    quant X -> X (1x128) and X^T (1x128 along M); quant W -> W and W^T
+  fwd    quant X -> X (1x128) and X^T (1x128 along M); quant W -> W
          (128x128); GEMM (1x128 x 128x128)                        -> Y  [M, N]
   bwd    quant dY -> dY (1x128) and dY^T (1x128 along M);
-         dgrad GEMM (dY x W^T)                                     -> dX [M, K]
+         quant W -> W^T (128x128); dgrad GEMM (dY x W^T)          -> dX [M, K]
          wgrad GEMM (dY^T x X^T, 1x128 x 1x128)                    -> dW [N, K]
 each call through the C ABI on torch's current stream.  HIP events around
 every launch give each kernel's average duration over the timed steps.
@@ -128,23 +128,27 @@ def step_plan(wl):
 
 
 def step_plan_dual(wl):
-    """The step as fp8_linear_fwd_save / fp8_linear_bwd enqueue it: each bf16
-    tensor read once, X -> X and X^T codes, W -> W and W^T codes, dY -> dY
-    and dY^T codes (fp8_blockwise_quant_dual, bit-identical to the separate
-    quantizers), then the three GEMMs."""
+    """The step as fp8_linear_fwd_save / fp8_linear_bwd enqueue it: X -> X
+    and X^T codes and dY -> dY and dY^T codes from one read each
+    (fp8_blockwise_quant_dual, bit-identical to the separate quantizers),
+    W -> W codes for the forward and W -> W^T codes right before the dgrad
+    GEMM, and the three GEMMs."""
     import blockwise_scaled_fp8_amd as fp8
     d = fp8.fp8_blockwise_quant_dual
+    q = fp8.fp8_blockwise_quant
     g = fp8.fp8_scaled_gemm_blockwise
     M, N, K = wl.M, wl.N, wl.K
     return [
         ("quant_dual X", lambda: d(wl.x, "1x128", q=wl.xq, recip=wl.xr, qt=wl.xtq, recip_t=wl.xtr),
          2 * M * K + 2 * M * K + 4 * (M * cdiv(K, 128) + K * cdiv(M, 128)), "B"),
-        ("quant_dual W", lambda: d(wl.w, "128x128", q=wl.wq, recip=wl.wr, qt=wl.wtq, recip_t=wl.wtr),
-         2 * N * K + 2 * N * K + 8 * cdiv(N, 128) * cdiv(K, 128), "B"),
+        ("quant_128x128 W", lambda: q(wl.w, "128x128", q=wl.wq, recip=wl.wr),
+         quant_bytes(N, K, "128x128"), "B"),
         ("gemm fwd", lambda: g(wl.xq, wl.xr, wl.wq, wl.wr, "128x128", out=wl.y),
          2 * M * N * K, "flop"),
         ("quant_dual dY", lambda: d(wl.dy, "1x128", q=wl.dyq, recip=wl.dyr, qt=wl.dytq, recip_t=wl.dytr),
          2 * M * N + 2 * M * N + 4 * (M * cdiv(N, 128) + N * cdiv(M, 128)), "B"),
+        ("quant_128x128^T W", lambda: q(wl.w, "128x128", transpose=True, q=wl.wtq, recip=wl.wtr),
+         quant_bytes(N, K, "128x128"), "B"),
         ("gemm dgrad", lambda: g(wl.dyq, wl.dyr, wl.wtq, wl.wtr, "128x128", out=wl.dx),
          2 * M * N * K, "flop"),
         ("gemm wgrad", lambda: g(wl.dytq, wl.dytr, wl.xtq, wl.xtr, "1x128", out=wl.dw),
@@ -700,7 +704,8 @@ def main():
         "data": "synthetic: X, dY ~ N(0,1) bf16; W ~ U(+-1/sqrt(K)) bf16 (nn.Linear init); seeded",
         "config": {"workload": "fp8 blockwise linear fwd+dgrad+wgrad incl. quantization",
                    "M": M, "N": N, "K": K, "recipes": "fwd/dgrad 1x128 x 128x128, wgrad 1x128 x 1x128",
-                   "quantization": "fused: each bf16 tensor read once into both code layouts",
+                   "quantization": "fused: X and dY each read once into both code layouts; "
+                                   "W into W codes in the forward and W^T codes right before dgrad",
                    "seed": args.seed},
         "roofline": {"bound": "mfma",
                      "kernel": f"{dominant.split()[1]} blockwise GEMM call "
@@ -711,8 +716,9 @@ def main():
         "gemm_tflops": {k: v["tflops"] for k, v in r["kernels"].items() if "tflops" in v},
         "quant_gbps": round(r["quant_gbps"], 1),
         "quant_frac_of_hbm_peak": round(r["quant_gbps"] / HBM_PEAK_GBS, 4),
-        "quant_note": "the three fused quantizer launches of the step: algorithmic bytes (bf16 read "
-                      "once, both code layouts and all scales written) / their event time",
+        "quant_note": "the four quantizer launches of the step (X and dY into both code layouts "
+                      "from one read, W into W and, in the backward, into W^T): algorithmic bytes "
+                      "(bf16 read, codes and scales written) / their event time",
         "kernels": r["kernels"],
         "wall_ms_per_step": round(r["wall_ms_per_step"], 4),
         "ms_per_step_with_call_events": round(r["gpu_ms_per_step_with_call_events"], 4),

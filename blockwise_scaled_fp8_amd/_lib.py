@@ -13,6 +13,8 @@ c_int = ctypes.c_int
 c_size = ctypes.c_size_t
 c_ptr = ctypes.c_void_p
 
+ABI_VERSION = 2   # fp8bw_abi_version() of the sources these prototypes mirror
+
 # name -> (restype, argtypes), mirroring include/fp8bw.h
 PROTOTYPES = {
     "fp8bw_abi_version": (c_int, []),
@@ -58,8 +60,8 @@ PROTOTYPES = {
     "fp8bw_linear_saved_bytes": (c_size, [c_i64, c_i64, c_i64]),
     "fp8_linear_fwd_save": (c_int, [c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr, c_size, c_ptr,
                                     c_size, c_ptr]),
-    "fp8_linear_bwd": (c_int, [c_ptr, c_ptr, c_size, c_ptr, c_ptr, c_i64, c_i64, c_i64, c_ptr,
-                               c_size, c_ptr]),
+    "fp8_linear_bwd": (c_int, [c_ptr, c_ptr, c_ptr, c_size, c_ptr, c_ptr, c_i64, c_i64, c_i64,
+                               c_ptr, c_size, c_ptr]),
 }
 
 STATUS = {0: "FP8BW_OK", 1: "FP8BW_ERR_NULL", 2: "FP8BW_ERR_SHAPE", 3: "FP8BW_ERR_LAYOUT",
@@ -93,6 +95,11 @@ def load_library():
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        # The prototypes above describe one version of the ABI; a library
+        # built from other sources would be called with the wrong arguments.
+        if lib.fp8bw_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{path} has ABI version {lib.fp8bw_abi_version()}, this binding "
+                               f"expects {ABI_VERSION}: rebuild it")
         _LIB = lib
     return _LIB
 

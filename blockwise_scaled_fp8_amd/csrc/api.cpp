@@ -91,7 +91,7 @@ size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
-FP8BW_API int fp8bw_abi_version(void) { return 1; }
+FP8BW_API int fp8bw_abi_version(void) { return 2; }
 
 FP8BW_API const char* fp8bw_status_str(int s) {
   switch (s) {
@@ -523,19 +523,23 @@ struct LinearLayout {
 };
 
 // Fused-quantization wrapper (fp8_linear_fwd_save / fp8_linear_bwd).
-// Saved buffer: [W^T codes K x N][W^T recip cdiv(K,128) x cdiv(N,128)]
-//               [X^T codes K x M][X^T recip K x cdiv(M,128)]
+// Saved buffer: [X^T codes K x M][X^T recip K x cdiv(M,128)]
 // fwd_save ws:  [X codes][W codes][X recip][W recip][fwd GEMM partials]
-// bwd ws:       [dY codes][dY^T codes][dY recip][dY^T recip][GEMM partials]
+// bwd ws:       [dY codes][dY^T codes][dY recip][dY^T recip]
+//               [W^T codes][W^T recip][GEMM partials]
+// W^T is quantized by the backward, right before the dgrad GEMM, rather than
+// kept from the forward: the GEMM then finds its freshly written B operand
+// in the chip's 256 MB memory-side cache (on the 16640 x 5120 x 8192 linear
+// step, dgrad 585 against 660 us, for 27 us of quantizer), and the saved
+// buffer holds only what the backward cannot recompute from its inputs.
 struct SavedLayout {
-  size_t wt_codes, wt_recip, xt_codes, xt_recip, total;
+  size_t xt_codes, xt_recip, total;
 };
 
 SavedLayout saved_layout(int64_t M, int64_t N, int64_t K) {
   SavedLayout S = {};
   size_t off = 0;
-  S.wt_codes = off; off += align_up((size_t)(K * N));
-  S.wt_recip = off; off += align_up((size_t)(cdiv(K, 128) * cdiv(N, 128)) * 4);
+  (void)N;
   S.xt_codes = off; off += align_up((size_t)(K * M));
   S.xt_recip = off; off += align_up((size_t)(K * cdiv(M, 128)) * 4);
   S.total = off;
@@ -544,7 +548,7 @@ SavedLayout saved_layout(int64_t M, int64_t N, int64_t K) {
 
 struct FusedLayout {
   size_t a_codes, a_codes_t, a_recip, a_recip_t, b_codes, b_recip, gemm_ws, total;
-};
+};   // bwd: b_codes / b_recip hold W^T
 
 FusedLayout fused_layout(int64_t M, int64_t N, int64_t K, int which) {
   FusedLayout F = {};
@@ -555,11 +559,13 @@ FusedLayout fused_layout(int64_t M, int64_t N, int64_t K, int which) {
     F.a_recip = off; off += align_up((size_t)(M * cdiv(K, 128)) * 4);
     F.b_recip = off; off += align_up((size_t)(cdiv(N, 128) * cdiv(K, 128)) * 4);
     F.gemm_ws = off; off += align_up(fp8bw_gemm_blockwise_ws_bytes(M, N, K));
-  } else {            // bwd: dY and dY^T codes for dgrad and wgrad
+  } else {            // bwd: dY and dY^T codes for dgrad and wgrad, W^T for dgrad
     F.a_codes = off; off += align_up((size_t)(M * N));
     F.a_codes_t = off; off += align_up((size_t)(N * M));
     F.a_recip = off; off += align_up((size_t)(M * cdiv(N, 128)) * 4);
     F.a_recip_t = off; off += align_up((size_t)(N * cdiv(M, 128)) * 4);
+    F.b_codes = off; off += align_up((size_t)(K * N));
+    F.b_recip = off; off += align_up((size_t)(cdiv(K, 128) * cdiv(N, 128)) * 4);
     F.gemm_ws = off;
     const size_t g1 = fp8bw_gemm_blockwise_ws_bytes(M, K, N), g2 = fp8bw_gemm_blockwise_ws_bytes(N, K, M);
     off += align_up(g1 > g2 ? g1 : g2);
@@ -720,7 +726,7 @@ FP8BW_API int fp8_linear_fwd_save(const void* x, const void* w, void* y, int64_t
   const FusedLayout F = fused_layout(M, N, K, 3);
   uint8_t* base = (uint8_t*)ws;
   uint8_t* sv = (uint8_t*)saved;
-  const int64_t nb = cdiv(N, 128), kbo = cdiv(K, 128);
+  const int64_t nb = cdiv(N, 128);
   uint8_t* xq = base + F.a_codes;
   uint8_t* wq = base + F.b_codes;
   float* xr = (float*)(base + F.a_recip);
@@ -730,18 +736,17 @@ FP8BW_API int fp8_linear_fwd_save(const void* x, const void* w, void* y, int64_t
   if ((st = fp8_blockwise_quant_dual(x, M, K, K, FP8BW_BLOCK_1x128, xq, K, xr, 1, M, sv + S.xt_codes,
                                      M, (float*)(sv + S.xt_recip), 1, K, stream)))
     return st;
-  // W: 128x128 codes (wr[nb_i + kb*nb]) and W^T (wtr[kb_i + nb_i*kbo]).
-  if ((st = fp8_blockwise_quant_dual(w, N, K, K, FP8BW_BLOCK_128x128, wq, K, wr, 1, nb, sv + S.wt_codes,
-                                     N, (float*)(sv + S.wt_recip), 1, kbo, stream)))
+  // W: 128x128 codes, wr[nb_i + kb*nb] (W^T is quantized by the backward).
+  if ((st = fp8_blockwise_quant(w, N, K, K, FP8BW_BLOCK_128x128, 0, wq, K, wr, 1, nb, stream)))
     return st;
   return fp8_scaled_gemm_blockwise(xq, K, xr, 1, M, wq, K, wr, 1, nb, FP8BW_BLOCK_128x128, M, N, K,
                                    y, N, FP8BW_OUT_BF16, base + F.gemm_ws, ws_bytes - F.gemm_ws, stream);
 }
 
-FP8BW_API int fp8_linear_bwd(const void* dy, const void* saved, size_t saved_bytes, void* dx,
-                             void* dw, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
-                             void* stream) {
-  int st = check_fused(dy, saved, M, N, K, saved, saved_bytes, ws, ws_bytes, 4);
+FP8BW_API int fp8_linear_bwd(const void* dy, const void* w, const void* saved, size_t saved_bytes,
+                             void* dx, void* dw, int64_t M, int64_t N, int64_t K, void* ws,
+                             size_t ws_bytes, void* stream) {
+  int st = check_fused(dy, w, M, N, K, saved, saved_bytes, ws, ws_bytes, 4);
   if (st != FP8BW_OK) return st;
   if (K == 0) return ok();
   if (M == 0) return dw ? zero_output(dw, N, K, stream) : ok();
@@ -758,16 +763,22 @@ FP8BW_API int fp8_linear_bwd(const void* dy, const void* saved, size_t saved_byt
   uint8_t* dytq = base + F.a_codes_t;
   float* dyr = (float*)(base + F.a_recip);
   float* dytr = (float*)(base + F.a_recip_t);
+  uint8_t* wtq = base + F.b_codes;
+  float* wtr = (float*)(base + F.b_recip);
   // dY: 1x128 along N (dyr[m + nb*M]) for dgrad and 1x128 along M
   // (dytr[n + mb*N]) for wgrad, from one read.
   if ((st = fp8_blockwise_quant_dual(dy, M, N, N, FP8BW_BLOCK_1x128, dyq, N, dyr, 1, M, dytq, M,
                                      dytr, 1, N, stream)))
     return st;
-  if (dx && (st = fp8_scaled_gemm_blockwise(dyq, N, dyr, 1, M, sv + S.wt_codes, N,
-                                            (const float*)(sv + S.wt_recip), 1, kbo,
-                                            FP8BW_BLOCK_128x128, M, K, N, dx, K, FP8BW_OUT_BF16,
-                                            base + F.gemm_ws, ws_bytes - F.gemm_ws, stream)))
-    return st;
+  if (dx) {
+    // W^T [K, N] codes, wtr[kb_i + nb_i*kbo], written just before their GEMM.
+    if ((st = fp8_blockwise_quant(w, N, K, K, FP8BW_BLOCK_128x128, 1, wtq, N, wtr, 1, kbo, stream)))
+      return st;
+    if ((st = fp8_scaled_gemm_blockwise(dyq, N, dyr, 1, M, wtq, N, wtr, 1, kbo, FP8BW_BLOCK_128x128,
+                                        M, K, N, dx, K, FP8BW_OUT_BF16, base + F.gemm_ws,
+                                        ws_bytes - F.gemm_ws, stream)))
+      return st;
+  }
   if (dw)
     return fp8_scaled_gemm_blockwise(dytq, M, dytr, 1, N, sv + S.xt_codes, M,
                                      (const float*)(sv + S.xt_recip), 1, K, FP8BW_BLOCK_1x128, N, K,

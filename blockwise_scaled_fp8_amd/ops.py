@@ -437,8 +437,8 @@ def fp8_linear_dgrad(dy, w, ws=None):
 @_on_tensor_device
 def fp8_linear_fwd_save(x, w, ws=None):
     """Y[M, N] = X . W^T with fused quantization: returns (Y, saved), where
-    saved (uint8, device) holds the X^T and W^T codes and scales that
-    fp8_linear_bwd needs (see include/fp8bw.h)."""
+    saved (uint8, device) holds the X^T codes and scales that fp8_linear_bwd
+    needs (see include/fp8bw.h)."""
     _bf16_2d(x, w)
     M, K = x.shape
     N = w.shape[0]
@@ -458,22 +458,25 @@ def fp8_linear_fwd_save(x, w, ws=None):
 
 
 @_on_tensor_device
-def fp8_linear_bwd(dy, saved, K, need_dx=True, need_dw=True, ws=None):
-    """(dX[M, K], dW[N, K]) from dY[M, N] and the saved buffer of
-    fp8_linear_fwd_save (dY quantized once); a gradient not needed is None."""
-    _bf16_2d(dy)
+def fp8_linear_bwd(dy, w, saved, need_dx=True, need_dw=True, ws=None):
+    """(dX[M, K], dW[N, K]) from dY[M, N], the forward's bf16 W[N, K] and
+    the saved buffer of fp8_linear_fwd_save (dY quantized once, W^T right
+    before the dgrad GEMM); a gradient not needed is None."""
+    _bf16_2d(dy, w)
     M, N = dy.shape
+    K = w.shape[1]
+    _check_shape(w, (N, K), "w")
     lib = load_library()
-    _need_cuda(dy, saved)
-    if not dy.is_contiguous():
-        raise ValueError("dy must be contiguous")
+    _need_cuda(dy, w, saved)
+    if not (dy.is_contiguous() and w.is_contiguous()):
+        raise ValueError("dy and w must be contiguous")
     if saved.dtype != torch.uint8 or saved.dim() != 1:
         raise ValueError("saved must be the 1-D uint8 buffer from fp8_linear_fwd_save")
     dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device) if need_dx else None
     dw = torch.empty((N, K), dtype=torch.bfloat16, device=dy.device) if need_dw else None
     if ws is None:
         ws = linear_workspace(M, N, K, 4, dy.device)
-    check(lib.fp8_linear_bwd(dy.data_ptr(), saved.data_ptr(), saved.numel(),
+    check(lib.fp8_linear_bwd(dy.data_ptr(), w.data_ptr(), saved.data_ptr(), saved.numel(),
                              dx.data_ptr() if dx is not None else None,
                              dw.data_ptr() if dw is not None else None, M, N, K, ws.data_ptr(),
                              ws.numel(), _stream(dy)))

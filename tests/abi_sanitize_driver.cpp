@@ -368,16 +368,16 @@ void linear_validation() {
         CHECK(known_status(fp8_linear_wgrad(buf_a, buf_b, buf_out, M, N, K, buf_ws, 0, nullptr)));
         CHECK(known_status(fp8_linear_fwd_save(buf_a, buf_b, buf_out, M, N, K, buf_ws, 0, buf_ws,
                                                0, nullptr)));
-        CHECK(known_status(fp8_linear_bwd(buf_a, buf_ws, 0, buf_out, buf_out, M, N, K, buf_ws, 0,
-                                          nullptr)));
+        CHECK(known_status(fp8_linear_bwd(buf_a, buf_b, buf_ws, 0, buf_out, buf_out, M, N, K,
+                                          buf_ws, 0, nullptr)));
       }
   EXPECT_STATUS(fp8_linear_fwd(buf_a, buf_b, buf_out, 128, 128, 128, buf_ws, 0, nullptr),
                 FP8BW_ERR_WORKSPACE);
   EXPECT_STATUS(fp8_linear_fwd(buf_a, buf_b, buf_out, 128, 128, 100, buf_ws, 0, nullptr),
                 FP8BW_ERR_SHAPE);
   EXPECT_STATUS(fp8_linear_fwd(buf_a, buf_b, buf_out, 0, 128, 128, nullptr, 0, nullptr), FP8BW_OK);
-  EXPECT_STATUS(fp8_linear_bwd(buf_a, buf_ws, 16, buf_out, buf_out, 128, 128, 128, buf_ws, 0,
-                               nullptr), FP8BW_ERR_WORKSPACE);
+  EXPECT_STATUS(fp8_linear_bwd(buf_a, buf_b, buf_ws, 16, buf_out, buf_out, 128, 128, 128, buf_ws,
+                               0, nullptr), FP8BW_ERR_WORKSPACE);
 }
 
 // fp8bw_last_error() is per thread: concurrent rejected calls each see their

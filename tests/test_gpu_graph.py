@@ -29,7 +29,7 @@ def _bits(t):
 
 def _step(x, w, dy, a, ra, b, rb, a2, ra2, b2, rb2, wg, rwg, ends):
     y, saved = fp8.fp8_linear_fwd_save(x, w)
-    dx, dw = fp8.fp8_linear_bwd(dy, saved, x.shape[1])
+    dx, dw = fp8.fp8_linear_bwd(dy, w, saved)
     xq, xr = fp8.fp8_tensorwise_quant(x)
     wq, wr = fp8.fp8_tensorwise_quant(w)
     yt = fp8.fp8_scaled_gemm_tensorwise(xq, xr, wq, wr)

@@ -120,8 +120,8 @@ def test_linear_shared_workspace_reuse(gpu):
 
 @pytest.mark.parametrize("mnk", [(384, 256, 640), (16640, 5120, 8192), (16640, 8192, 5120)])
 def test_fused_quant_linear_matches_separate(gpu, mnk):
-    """fp8_linear_fwd_save + fp8_linear_bwd (each bf16 tensor quantized once
-    into both layouts) give bit-identical Y, dX and dW to the three separate
+    """fp8_linear_fwd_save + fp8_linear_bwd (X and dY each quantized once
+    into both layouts, W^T quantized by the backward) give bit-identical Y, dX and dW to the three separate
     entry points, whose results the tests above check against the oracle;
     a skipped gradient leaves the other unchanged."""
     M, N, K = mnk
@@ -131,13 +131,13 @@ def test_fused_quant_linear_matches_separate(gpu, mnk):
     dx_ref = fp8.fp8_linear_dgrad(dy, w)
     dw_ref = fp8.fp8_linear_wgrad(dy, x)
     y, saved = fp8.fp8_linear_fwd_save(x, w)
-    dx, dw = fp8.fp8_linear_bwd(dy, saved, K)
+    dx, dw = fp8.fp8_linear_bwd(dy, w, saved)
     torch.cuda.synchronize()
     assert torch.equal(y, y_ref), "fused fwd differs from fp8_linear_fwd"
     assert torch.equal(dx, dx_ref), "fused dgrad differs from fp8_linear_dgrad"
     assert torch.equal(dw, dw_ref), "fused wgrad differs from fp8_linear_wgrad"
-    dx2, none_dw = fp8.fp8_linear_bwd(dy, saved, K, need_dx=True, need_dw=False)
-    none_dx, dw2 = fp8.fp8_linear_bwd(dy, saved, K, need_dx=False, need_dw=True)
+    dx2, none_dw = fp8.fp8_linear_bwd(dy, w, saved, need_dx=True, need_dw=False)
+    none_dx, dw2 = fp8.fp8_linear_bwd(dy, w, saved, need_dx=False, need_dw=True)
     torch.cuda.synchronize()
     assert none_dw is None and none_dx is None
     assert torch.equal(dx2, dx_ref) and torch.equal(dw2, dw_ref)
@@ -166,10 +166,10 @@ def test_fused_linear_canaries(gpu):
     say("fused linear canaries")
     check(lib.fp8_linear_fwd_save(x.data_ptr(), w.data_ptr(), yb.data_ptr(), M, N, K,
                                   saved.data_ptr(), saved_bytes, wsf.data_ptr(), ws_f, stream))
-    check(lib.fp8_linear_bwd(dy.data_ptr(), saved.data_ptr(), saved_bytes, dxb.data_ptr(),
-                             dwb.data_ptr(), M, N, K, wsb.data_ptr(), ws_b, stream))
+    check(lib.fp8_linear_bwd(dy.data_ptr(), w.data_ptr(), saved.data_ptr(), saved_bytes,
+                             dxb.data_ptr(), dwb.data_ptr(), M, N, K, wsb.data_ptr(), ws_b, stream))
     y_ref, saved_ref = fp8.fp8_linear_fwd_save(x, w)
-    dx_ref, dw_ref = fp8.fp8_linear_bwd(dy, saved_ref, K)
+    dx_ref, dw_ref = fp8.fp8_linear_bwd(dy, w, saved_ref)
     torch.cuda.synchronize()
     for buf, n, name in ((saved, saved_bytes, "saved"), (wsf, ws_f, "fwd workspace"),
                          (wsb, ws_b, "bwd workspace"), (yb, 2 * M * N, "y"),
@@ -194,4 +194,4 @@ def test_fused_forward_ragged_tokens(gpu, mnk):
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
     with pytest.raises(fp8.FP8BWError, match="multiples of 128"):
-        fp8.fp8_linear_bwd(dy, saved, K)
+        fp8.fp8_linear_bwd(dy, w, saved)

@@ -33,9 +33,9 @@ def test_fused_fake_shapes():
     y, saved = torch.ops.fp8bw.linear_fwd_save(x, w)
     assert y.shape == (256, 384) and saved.dtype == torch.uint8 and saved.dim() == 1
     assert saved.numel() == fp8.linear_saved_bytes(256, 384, 512)
-    dx, dw = torch.ops.fp8bw.linear_bwd(dy, saved, 512, True, True)
+    dx, dw = torch.ops.fp8bw.linear_bwd(dy, w, saved, True, True)
     assert dx.shape == (256, 512) and dw.shape == (384, 512)
-    dx, dw = torch.ops.fp8bw.linear_bwd(dy, saved, 512, False, True)
+    dx, dw = torch.ops.fp8bw.linear_bwd(dy, w, saved, False, True)
     assert dx.numel() == 0 and dw.shape == (384, 512)
 
 
