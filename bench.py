@@ -130,16 +130,18 @@ def step_plan(wl):
 def step_plan_dual(wl):
     """The step as fp8_linear_fwd_save / fp8_linear_bwd enqueue it: X -> X
     and X^T codes and dY -> dY and dY^T codes from one read each
-    (fp8_blockwise_quant_dual, bit-identical to the separate quantizers),
-    W -> W codes for the forward and W -> W^T codes right before the dgrad
-    GEMM, and the three GEMMs."""
+    (fp8_blockwise_quant_dual, bit-identical to the separate quantizers; X^T,
+    kept for the backward, with nontemporal stores), W -> W codes for the
+    forward and W -> W^T codes right before the dgrad GEMM, and the three
+    GEMMs."""
     import blockwise_scaled_fp8_amd as fp8
     d = fp8.fp8_blockwise_quant_dual
     q = fp8.fp8_blockwise_quant
     g = fp8.fp8_scaled_gemm_blockwise
     M, N, K = wl.M, wl.N, wl.K
     return [
-        ("quant_dual X", lambda: d(wl.x, "1x128", q=wl.xq, recip=wl.xr, qt=wl.xtq, recip_t=wl.xtr),
+        ("quant_dual X", lambda: d(wl.x, "1x128", q=wl.xq, recip=wl.xr, qt=wl.xtq, recip_t=wl.xtr,
+                                   stream_t=True),
          2 * M * K + 2 * M * K + 4 * (M * cdiv(K, 128) + K * cdiv(M, 128)), "B"),
         ("quant_128x128 W", lambda: q(wl.w, "128x128", q=wl.wq, recip=wl.wr),
          quant_bytes(N, K, "128x128"), "B"),

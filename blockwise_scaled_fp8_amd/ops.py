@@ -137,10 +137,12 @@ def fp8_blockwise_quant(x, block="1x128", transpose=False, q=None, recip=None):
 
 
 @_on_tensor_device
-def fp8_blockwise_quant_dual(x, block="1x128", q=None, recip=None, qt=None, recip_t=None):
+def fp8_blockwise_quant_dual(x, block="1x128", q=None, recip=None, qt=None, recip_t=None,
+                             stream_t=False):
     """Both layouts from one read of x: returns (q, recip, qt, recip_t), equal
     to fp8_blockwise_quant(x, block) and fp8_blockwise_quant(x, block,
-    transpose=True)."""
+    transpose=True).  stream_t writes qt with nontemporal stores (codes read
+    only much later; the same bits)."""
     lib = load_library()
     _need_cuda(x)
     _rowmajor(x, "x")
@@ -165,7 +167,7 @@ def fp8_blockwise_quant_dual(x, block="1x128", q=None, recip=None, qt=None, reci
                                        q.data_ptr(), q.stride(0), recip.data_ptr(), recip.stride(0),
                                        recip.stride(1), qt.data_ptr(), qt.stride(0),
                                        recip_t.data_ptr(), recip_t.stride(0), recip_t.stride(1),
-                                       _stream(x)))
+                                       1 if stream_t else 0, _stream(x)))
     return q, recip, qt, recip_t
 
 

@@ -131,13 +131,18 @@ int fp8_blockwise_quant(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
  *            rb*rst_kb] (the same values in the other index order).
  *   q, qt    device E4M3 [rows, cols] (ld_q >= cols) and [cols, rows]
  *            (ld_qt >= rows); the two must not overlap (checked).
+ *   stream_t nonzero: qt is written with nontemporal stores, which keep the
+ *            transposed codes from evicting the caches' contents (for codes
+ *            read only much later, such as the X^T a training forward keeps
+ *            for its backward, while q feeds the GEMM that runs next).  The
+ *            same bits either way.
  *   Requires cols % 16 == 0 and rows % 16 == 0; each output is validated as
  *   in fp8_blockwise_quant, and results are bit-identical to two calls of it.
  */
 int fp8_blockwise_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int block,
                              void* q, int64_t ld_q, float* recip, int64_t rs_row, int64_t rs_kb,
                              void* qt, int64_t ld_qt, float* recip_t, int64_t rst_row,
-                             int64_t rst_kb, void* stream);
+                             int64_t rst_kb, int stream_t, void* stream);
 
 /*
  * fp8_tensorwise_quant -- one scale for the whole tensor ([AITER]

@@ -107,11 +107,11 @@ void quant_validation() {
                                     kI64Max - 15, buf_s, 1, 1, nullptr), FP8BW_ERR_HIP);
   // Dual: overlapping code buffers; and extreme strides on the second output.
   EXPECT_STATUS(fp8_blockwise_quant_dual(buf_a, 128, 128, 128, FP8BW_BLOCK_1x128, buf_out, 128,
-                                         buf_s, 1, 128, buf_out + 64, 128, buf_s + 512, 1, 128,
+                                         buf_s, 1, 128, buf_out + 64, 128, buf_s + 512, 1, 128, 0,
                                          nullptr), FP8BW_ERR_LAYOUT);
   EXPECT_STATUS(fp8_blockwise_quant_dual(buf_a, 128, 128, 128, FP8BW_BLOCK_1x128, buf_out, 128,
                                          buf_s, 1, 128, buf_b, kI64Max - 15, buf_s + 512, 1, 128,
-                                         nullptr), FP8BW_ERR_LAYOUT);
+                                         1, nullptr), FP8BW_ERR_LAYOUT);
 
   // Sweep: every combination of extreme sizes and strides returns a known
   // status without undefined behaviour.
@@ -140,7 +140,8 @@ void quant_validation() {
       for (int64_t ld : kStrides) {
         CHECK(known_status(fp8_blockwise_quant_dual(buf_a, rows, cols, ld, FP8BW_BLOCK_1x128,
                                                     buf_out, ld, buf_s, 1, ld, buf_b, ld,
-                                                    buf_s + 512, 1, ld, nullptr)));
+                                                    buf_s + 512, 1, ld, (int)(ld & 1),
+                                                    nullptr)));
       }
 }
 

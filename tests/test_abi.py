@@ -75,11 +75,12 @@ def test_quant_validation(lib):
 
 def _dual(lib, **kw):
     a = dict(x=P, rows=64, cols=256, ld_x=256, block=0, q=P, ld_q=256, recip=P, rs_row=1,
-             rs_kb=64, qt=P + (1 << 20), ld_qt=64, recip_t=P, rst_row=1, rst_kb=256, stream=None)
+             rs_kb=64, qt=P + (1 << 20), ld_qt=64, recip_t=P, rst_row=1, rst_kb=256, stream_t=0,
+             stream=None)
     a.update(kw)
     return lib.fp8_blockwise_quant_dual(*[a[k] for k in (
         "x", "rows", "cols", "ld_x", "block", "q", "ld_q", "recip", "rs_row", "rs_kb", "qt",
-        "ld_qt", "recip_t", "rst_row", "rst_kb", "stream")])
+        "ld_qt", "recip_t", "rst_row", "rst_kb", "stream_t", "stream")])
 
 
 def test_dual_quant_validation(lib):

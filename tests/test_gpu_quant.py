@@ -148,7 +148,11 @@ def test_quant_dual_layouts(gpu, block, shape):
         q, r, qt, rt = fp8.fp8_blockwise_quant_dual(xd, block)
         q1, r1 = fp8.fp8_blockwise_quant(xd, block)
         q2, r2 = fp8.fp8_blockwise_quant(xd, block, transpose=True)
+        # nontemporal stores of the transposed codes: the same bits
+        streamed = fp8.fp8_blockwise_quant_dual(xd, block, stream_t=True)
         torch.cuda.synchronize()
+        for a, b in zip(streamed, (q, r, qt, rt)):   # codes, and positive finite scales
+            assert torch.equal(a, b), f"dual {block} {what} {shape}: stream_t changed the result"
         if block == "1x128":
             oq, orc = quant.quant_1x128(bits(x))
             oqt, ort = quant.quant_1x128_along_rows(bits(x))
@@ -224,9 +228,11 @@ def test_quant_outputs_stay_in_bounds_and_honour_strides(gpu):
     assert_f32_equal(host_f32(rt), orc, "canary T recip")
 
 
+@pytest.mark.parametrize("stream_t", [False, True])
 @pytest.mark.parametrize("block", ["1x128", "128x128"])
-def test_quant_dual_outputs_stay_in_bounds(gpu, block):
-    """Both layouts of the dual quantizer written into canary-padded code
+def test_quant_dual_outputs_stay_in_bounds(gpu, block, stream_t):
+    """Both layouts of the dual quantizer (transposed codes with plain or
+    nontemporal stores) written into canary-padded code
     buffers (ld > width) and strided views of NaN-filled scale buffers, from
     a 208 x 384 input (a partly filled last row block): bit-exact against
     the oracle, and nothing outside the logical regions changes."""
@@ -239,9 +245,9 @@ def test_quant_dual_outputs_stay_in_bounds(gpu, block):
     qtbuf = torch.full((cols, rows + 48), 0x5A, dtype=torch.uint8, device=gpu)
     rbuf = torch.full((ni, nj + 2), float("nan"), dtype=torch.float32, device=gpu)
     rtbuf = torch.full((ti, tj + 3), float("nan"), dtype=torch.float32, device=gpu)
-    say("quant dual canary", block)
+    say("quant dual canary", block, "stream_t" if stream_t else "")
     fp8.fp8_blockwise_quant_dual(xd, block, q=qbuf[:, :cols], recip=rbuf[:, :nj],
-                                 qt=qtbuf[:, :rows], recip_t=rtbuf[:, :tj])
+                                 qt=qtbuf[:, :rows], recip_t=rtbuf[:, :tj], stream_t=stream_t)
     torch.cuda.synchronize()
     if block == "1x128":
         oq, orc = quant.quant_1x128(bits(x))
