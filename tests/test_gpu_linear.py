@@ -195,3 +195,21 @@ def test_fused_forward_ragged_tokens(gpu, mnk):
     assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
     with pytest.raises(fp8.FP8BWError, match="multiples of 128"):
         fp8.fp8_linear_bwd(dy, w, saved)
+
+
+@pytest.mark.parametrize("mnk", [(384, 256, 640), (16640, 5120, 8192)])
+def test_bench_step_is_the_training_pair(gpu, mnk):
+    """The launches bench.py times one by one as the step (its step plan)
+    produce exactly what fp8_linear_fwd_save + fp8_linear_bwd produce: the
+    timed sequence is the training pair, call for call."""
+    import bench
+    M, N, K = mnk
+    say("bench step plan vs training pair", mnk)
+    wl = bench.Workload(3, gpu, shape=(M, N, K))
+    for _, fn, _, _ in bench.step_plan_dual(wl):
+        fn()
+    y, saved = fp8.fp8_linear_fwd_save(wl.x, wl.w)
+    dx, dw = fp8.fp8_linear_bwd(wl.dy, wl.w, saved)
+    torch.cuda.synchronize()
+    for got, ref, name in ((wl.y, y, "Y"), (wl.dx, dx, "dX"), (wl.dw, dw, "dW")):
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"{name} {mnk} differs"
