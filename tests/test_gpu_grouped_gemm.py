@@ -146,3 +146,30 @@ def test_grouped_benchmark_configuration_sampled(gpu):
     starts = np.r_[0, ends[:-1]]
     sample = np.unique(np.r_[starts, ends - 1, rng.integers(0, M, 16)])
     _case(gpu, G, M, N, K, ends, "bf16", seed=55, sample=sample)
+
+
+@pytest.mark.parametrize("od", ["bf16", "f32"])
+def test_grouped_large_tiles_ragged_windows(gpu, od):
+    """More than two rounds of 256x256 tiles on a group table whose groups
+    end at every kind of offset inside a tile: a group's last tile loads a
+    window that runs past the group's end (or, at the end of A, starts
+    before the tile) and stores only its own rows; groups of 129-255
+    leftover rows stay on the large tiles, an empty group, a first group
+    whose last tile reaches into the next group.  Sampled rows: every
+    group's first and last rows, the rows around each 256-row tile boundary
+    inside a group, and random ones."""
+    sizes = [3 * 256 + 200, 255, 129, 5 * 256 + 1, 0, 8 * 256 + 130, 2 * 256 + 250,
+             4 * 256 + 64, 300]
+    ends = np.cumsum(sizes)
+    M = int(ends[-1])
+    starts = np.r_[0, ends[:-1]]
+    rng = np.random.default_rng(60)
+    rows = [0, M - 1]
+    for s0, n in zip(starts, sizes):
+        if n == 0:
+            continue
+        rows += [s0, s0 + n - 1]
+        for t in range(256, n, 256):
+            rows += [s0 + t - 1, s0 + t]
+    sample = np.unique(np.r_[rows, rng.integers(0, M, 40)])
+    _case(gpu, len(sizes), M, 4096, 256, list(ends), od, seed=60, sample=sample)
