@@ -366,7 +366,9 @@ int fp8_linear_wgrad(const void* dy, const void* x, void* dw, int64_t M, int64_t
  * / _wgrad (bit-identical outputs), with fused quantization
  * (fp8_blockwise_quant_dual): the forward quantizes X once into X (1x128
  * along K) and X^T (1x128 along M), keeping X^T's codes and scales for the
- * backward, and W into W (128x128); the backward quantizes dY once into dY
+ * backward (written with nontemporal stores, so that X's codes stay cached
+ * for the forward GEMM), and W into W (128x128); the backward quantizes dY
+ * once into dY
  * and dY^T, and W into W^T right before the dgrad GEMM.  The quantizers are
  * the part of the fp8 linear step the pages single out as slow ([INTEG]
  * Benchmarks); fp8 X^T codes are also half the size of the bf16 X a

@@ -1,8 +1,8 @@
 """HIP graph capture of the hot path.
 
 Captured into one graph: the fused training step (fp8_linear_fwd_save +
-fp8_linear_bwd: three dual quantizers and three GEMMs), the per-tensor path
-(two-kernel quantizer, tensorwise GEMM), a whole-problem split-K GEMM
+fp8_linear_bwd: two dual quantizers, the W and W^T quantizers and three
+GEMMs), the per-tensor path (two-kernel quantizer, tensorwise GEMM), a whole-problem split-K GEMM
 (partials + ordered reduce), a 272-tile GEMM (full rounds of 256x256 tiles,
 then the leftover tiles split over K and reduced) and a grouped GEMM whose
 group boundaries are read on the device.  No library call records a
