@@ -18,11 +18,19 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
+// fp32 -> bf16, round to nearest even, in hardware: gfx950's
+// v_cvt_pk_bf16_f32 converts a pair in one instruction (the same bits as
+// rounding the fp32 pattern by hand for every finite input, at a fifth of
+// the VALU work, which the GEMM epilogues pay for every output element).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// One value: bf16 bits in the low half.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return pack_bf16x2_rne(f, 0.f) & 0xFFFFu;
 }
 
 // Scale from a block amax: s = 448 / max(amax, eps), IEEE fp32 division

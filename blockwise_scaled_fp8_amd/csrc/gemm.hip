@@ -29,6 +29,7 @@
 //    in split order (deterministic, no atomics).
 
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -566,8 +567,8 @@ __device__ __forceinline__ void store_acc(const GemmArgs& p, const v4f (&acc)[TM
               make_float4(val[0], val[1], val[2], val[3]);
         } else if constexpr (OUT == kOutBf16) {
           uint2 w;
-          w.x = f32_to_bf16_rne(val[0]) | (f32_to_bf16_rne(val[1]) << 16);
-          w.y = f32_to_bf16_rne(val[2]) | (f32_to_bf16_rne(val[3]) << 16);
+          w.x = pack_bf16x2_rne(val[0], val[1]);
+          w.y = pack_bf16x2_rne(val[2], val[3]);
           *(uint2*)((uint16_t*)p.out + (int64_t)m * p.ldo + nq) = w;
         } else {
           *(float4*)((float*)p.out + (int64_t)m * p.ldo + nq) =
@@ -625,27 +626,42 @@ __device__ __forceinline__ void store_tile_bf16_lds(const GemmArgs& p, const v4f
   // (On gfx950 a workgroup-scope fence waits for LDS accesses only, so the
   // barriers below leave the storing waves' global stores in flight.)
   __syncthreads();   // every wave is done reading the stages
+  // The lane's 16 columns are the same in every sub-tile row: their bias
+  // values are read once, and without a bias nothing is added.
+  auto write_tile = [&](auto with_bias) {
+    constexpr bool kBias = decltype(with_bias)::value;
+    float bv[TN][4];
+    if constexpr (kBias) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    uint8_t* const qb = arr(2 * wmi + i / 4);
-    const int rq = 16 * (i % 4) + frow;
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int nq = n0 + 64 * wni + 16 * j + 4 * fhalf;
-      float val[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        val[v] = acc[i][j][v];
-        if constexpr (MODE == kTensorwise) val[v] *= tscale;
-        val[v] += bias_at(p.bias, nq + v);
-      }
-      u32x2 w;
-      w.x = f32_to_bf16_rne(val[0]) | (f32_to_bf16_rne(val[1]) << 16);
-      w.y = f32_to_bf16_rne(val[2]) | (f32_to_bf16_rne(val[3]) << 16);
-      const int chunk = 8 * wni + 2 * j + (fhalf >> 1);
-      *(u32x2*)(qb + rq * 512 + 16 * (chunk ^ frow) + 8 * (fhalf & 1)) = w;
+        for (int v = 0; v < 4; ++v) bv[j][v] = bf16lo(p.bias[n0 + 64 * wni + 16 * j + 4 * fhalf + v]);
     }
-  }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      uint8_t* const qb = arr(2 * wmi + i / 4);
+      const int rq = 16 * (i % 4) + frow;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        float val[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          val[v] = acc[i][j][v];
+          if constexpr (MODE == kTensorwise) val[v] *= tscale;
+          if constexpr (kBias) val[v] += bv[j][v];
+        }
+        u32x2 w;
+        w.x = pack_bf16x2_rne(val[0], val[1]);
+        w.y = pack_bf16x2_rne(val[2], val[3]);
+        const int chunk = 8 * wni + 2 * j + (fhalf >> 1);
+        *(u32x2*)(qb + rq * 512 + 16 * (chunk ^ frow) + 8 * (fhalf & 1)) = w;
+      }
+    }
+  };
+  if (p.bias)
+    write_tile(std::true_type{});
+  else
+    write_tile(std::false_type{});
   const int c = lane & 31;
   __syncthreads();
   if constexpr (STORERS0 > 0) {
@@ -1249,8 +1265,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
       if (vec) {
         if (OUT == kOutBf16) {
           uint2 w;
-          w.x = f32_to_bf16_rne(val[0]) | (f32_to_bf16_rne(val[1]) << 16);
-          w.y = f32_to_bf16_rne(val[2]) | (f32_to_bf16_rne(val[3]) << 16);
+          w.x = pack_bf16x2_rne(val[0], val[1]);
+          w.y = pack_bf16x2_rne(val[2], val[3]);
           *(uint2*)((uint16_t*)out + m * ldo + n) = w;
         } else {
           *(float4*)((float*)out + m * ldo + n) = make_float4(val[0], val[1], val[2], val[3]);
@@ -1332,8 +1348,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_tiled_kernel(
     if (vec && n + 3 < N) {
       if (OUT == kOutBf16) {
         uint2 w;
-        w.x = f32_to_bf16_rne(val[0]) | (f32_to_bf16_rne(val[1]) << 16);
-        w.y = f32_to_bf16_rne(val[2]) | (f32_to_bf16_rne(val[3]) << 16);
+        w.x = pack_bf16x2_rne(val[0], val[1]);
+        w.y = pack_bf16x2_rne(val[2], val[3]);
         *(uint2*)((uint16_t*)out + (int64_t)m * ldo + n) = w;
       } else {
         *(float4*)((float*)out + (int64_t)m * ldo + n) = make_float4(val[0], val[1], val[2], val[3]);

@@ -506,3 +506,34 @@ def test_tensorwise_bias_epilogue(gpu, mnk, od):
     ref = gemm.add_bias(gemm.tensorwise_gemm(xq, xr, wq, wr), bias)
     S = gemm.tensorwise_bound(xq, xr, wq, wr) + np.abs(e4m3.bf16_bits_to_f32(bias))[None, :]
     check_gemm_output(host_f32(out), ref, S, -(-K // 128), od, f"tensorwise bias {mnk}")
+
+
+@pytest.mark.parametrize("shape", ["persistent_leftover", "ragged_small_tiles", "whole_split"])
+def test_bf16_output_is_rne_of_the_fp32_output(gpu, shape):
+    """Every bf16 store path rounds its fp32 value to nearest even: the bf16
+    output of a GEMM equals, bit for bit on every element, the host's RNE of
+    the fp32 output of the same GEMM (same plan, same accumulation order):
+    the persistent launch's staged epilogue and its leftover tiles' reduce,
+    the small-tile kernel's direct stores at ragged edges, and the
+    whole-problem split-K reduce."""
+    cus = torch.cuda.get_device_properties(gpu).multi_processor_count
+    M, N, K = {"persistent_leftover": (4352, 32 * cus, 2048),
+               "ragged_small_tiles": (300, 200, 512),
+               "whole_split": (512, 512, 16384)}[shape]
+    kb = K // 128
+    rng = np.random.default_rng(70 + len(shape))
+    aq, bq = _random_codes(rng, (M, K)), _random_codes(rng, (N, K))
+    ar = rng.uniform(0.01, 0.02, (M, kb)).astype(np.float32)
+    br = rng.uniform(0.01, 0.02, (-(-N // 128), kb)).astype(np.float32)
+    a_d, b_d = _up_codes(aq, gpu), _up_codes(bq, gpu)
+    ra_d, rb_d = _up_scales_colmajor(ar, gpu), _up_scales_colmajor(br, gpu)
+    say("bf16 = RNE(fp32)", shape, M, N, K, fp8.gemm_plan(M, N, K))
+    outs = {}
+    for od in (torch.float32, torch.bfloat16):
+        outs[od] = fp8.fp8_scaled_gemm_blockwise(a_d, ra_d, b_d, rb_d, "128x128", out_dtype=od)
+    torch.cuda.synchronize()
+    want = e4m3.f32_to_bf16_bits(outs[torch.float32].cpu().numpy())
+    got = outs[torch.bfloat16].cpu().view(torch.int16).numpy().view(np.uint16)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, (f"{shape}: {bad[0].size} bf16 outputs differ from RNE of the fp32 "
+                              f"output, first at {tuple(b[0] for b in bad)}")
