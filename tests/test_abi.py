@@ -265,3 +265,16 @@ def test_no_host_fallback_in_binding():
     with pytest.raises(ValueError):
         fp8.fp8_blockwise_quant(x)
     assert ctypes.sizeof(ctypes.c_void_p) == 8
+
+
+def test_binding_refuses_a_library_of_another_abi_version(monkeypatch):
+    """The ctypes prototypes describe one ABI version: a library reporting
+    another one is refused at load, instead of being called with the wrong
+    arguments."""
+    from blockwise_scaled_fp8_amd import _lib as lib_mod
+    monkeypatch.setattr(lib_mod, "_LIB", None)
+    monkeypatch.setattr(lib_mod, "ABI_VERSION", lib_mod.ABI_VERSION + 1)
+    with pytest.raises(RuntimeError, match="ABI version"):
+        lib_mod.load_library()
+    monkeypatch.undo()
+    assert lib_mod.load_library().fp8bw_abi_version() == lib_mod.ABI_VERSION
